@@ -1,0 +1,36 @@
+// launch.h - internal launchers behind the C ABI (arguments already
+// validated on the host by mxq_api.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+hipError_t launch_quantize_per_tensor(const void* x, int src, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                                      float* history, int hist_len, float* amax_out, float* scale_out,
+                                      float* scale_inv_out, uint8_t* q_row, uint8_t* q_col, hipStream_t st);
+
+hipError_t launch_quantize_mx(const void* x, int src, int64_t rows, int64_t cols, int64_t ld, int fmt, uint8_t* q_row,
+                              uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t st);
+
+hipError_t launch_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const int32_t* idx, int64_t src_rows,
+                                    int64_t rows, int64_t cols, uint8_t* q8, uint8_t* s8, hipStream_t st);
+
+// Dense (group_off == nullptr) or grouped scaled GEMM.
+struct GemmArgs {
+    const uint8_t* A;
+    const void* sA;
+    const uint8_t* B;
+    const void* sB;
+    void* C;
+    const int64_t* group_off;  // device [G+1] or nullptr
+    int64_t G;
+    int64_t M, N, K;  // M = total rows for the grouped form
+    int64_t ldc;
+    int64_t b_group_stride;  // bytes between consecutive B_g
+    int64_t sb_group_stride; // bytes between consecutive sB_g (0 for per-tensor)
+    int fa, fb, ma, mb, out;
+};
+hipError_t launch_scaled_gemm(const GemmArgs& a, hipStream_t st);
+
+}  // namespace mxq

@@ -1,0 +1,123 @@
+"""The C-ABI library loads, exports every function include/mxq.h declares, and
+rejects invalid arguments on the host (no GPU needed: validation happens
+before any HIP call, and these calls never pass it, or are zero-size)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+OK, ENULL, ESHAPE, EALIGN, EFMT = 0, -1, -2, -3, -4
+P = 0x10000  # a 16-byte aligned stand-in address: never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def L():
+    import mxfp4_precision_numerics_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from mxfp4_precision_numerics_amd import build
+        build.build()
+    return m.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mxq_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status(L):
+    assert L.mxq_abi_version() == 1
+    for st in (OK, ENULL, ESHAPE, EALIGN, EFMT, -5):
+        assert L.mxq_status_string(st)
+    assert L.mxq_status_string(-99) == b"unknown status"
+
+
+def qpt(L, **kw):
+    a = dict(x=P, src=1, rows=32, cols=64, ld=64, fmt=0, hist=None, hl=0, amax=P, scale=P, sinv=P,
+             q_row=P, q_col=None)
+    a.update(kw)
+    return L.mxq_quantize_per_tensor(a["x"], a["src"], a["rows"], a["cols"], a["ld"], a["fmt"], a["hist"], a["hl"],
+                                     a["amax"], a["scale"], a["sinv"], a["q_row"], a["q_col"], None)
+
+
+def test_quantize_per_tensor_validation(L):
+    assert qpt(L, fmt=2) == EFMT                      # E2M1 has no per-tensor path
+    assert qpt(L, src=3) == EFMT
+    assert qpt(L, x=None) == ENULL
+    assert qpt(L, amax=None) == ENULL
+    assert qpt(L, q_row=None, q_col=None) == ENULL
+    assert qpt(L, hl=16, hist=None) == ENULL
+    assert qpt(L, cols=60, ld=60) == ESHAPE
+    assert qpt(L, ld=32) == ESHAPE
+    assert qpt(L, q_col=P, rows=40) == ESHAPE
+    assert qpt(L, rows=-1) == ESHAPE
+    assert qpt(L, hl=2000, hist=P) == ESHAPE
+    assert qpt(L, x=P + 8) == EALIGN
+    assert qpt(L, ld=68) == EALIGN                     # 68 * 2 bytes is not a multiple of 16
+    assert qpt(L, rows=0) == OK                        # zero-size: no launch
+    assert qpt(L, cols=0, ld=0) == OK
+
+
+def qmx(L, **kw):
+    a = dict(x=P, src=1, rows=64, cols=64, ld=64, fmt=0, q_row=P, s_row=P, q_col=None, s_col=None)
+    a.update(kw)
+    return L.mxq_quantize_mx(a["x"], a["src"], a["rows"], a["cols"], a["ld"], a["fmt"], a["q_row"], a["s_row"],
+                             a["q_col"], a["s_col"], None)
+
+
+def test_quantize_mx_validation(L):
+    assert qmx(L, fmt=7) == EFMT
+    assert qmx(L, fmt=2, q_col=P, s_col=P) == EFMT     # no colwise E2M1
+    assert qmx(L, s_row=None) == ENULL
+    assert qmx(L, q_col=P, s_col=None) == ENULL
+    assert qmx(L, cols=48, ld=48) == ESHAPE
+    assert qmx(L, q_col=P, s_col=P, rows=48) == ESHAPE
+    assert qmx(L, s_row=P + 1) == EALIGN
+    assert qmx(L, rows=0) == OK
+
+
+def test_repack_validation(L):
+    f = L.mxq_repack_fp4_to_fp8
+    assert f(P, P, None, 4, 4, 100, P, P, None) == ESHAPE      # cols % 128
+    assert f(P, P, None, 4, 5, 128, P, P, None) == ESHAPE      # rows > src_rows without gather
+    assert f(None, P, None, 4, 4, 128, P, P, None) == ENULL
+    assert f(P, P, P + 2, 4, 4, 128, P, P, None) == EALIGN
+    assert f(P, P, P, 4, 0, 128, P, P, None) == OK
+
+
+def test_gemm_validation(L):
+    g = L.mxq_scaled_gemm
+    assert g(P, 0, P, 1, P, 0, P, 1, 16, 16, 100, P, 0, 16, None) == ESHAPE   # K % 128
+    assert g(P, 0, P, 1, P, 0, P, 1, 16, 16, 0, P, 0, 16, None) == ESHAPE     # K = 0
+    assert g(P, 3, P, 1, P, 0, P, 1, 16, 16, 128, P, 0, 16, None) == EFMT
+    assert g(P, 0, P, 5, P, 0, P, 1, 16, 16, 128, P, 0, 16, None) == EFMT
+    assert g(P, 0, P, 1, P, 0, P, 1, 16, 16, 128, P, 2, 16, None) == EFMT    # out type
+    assert g(P, 0, None, 1, P, 0, P, 1, 16, 16, 128, P, 0, 16, None) == ENULL
+    assert g(P, 0, P, 1, P, 0, P, 1, 16, 16, 128, P, 0, 8, None) == ESHAPE    # ldc < N
+    assert g(P, 0, P, 1, P, 0, P, 1, 16, 18, 128, P, 0, 18, None) == EALIGN   # ldc*4 % 16
+    assert g(P + 4, 0, P, 1, P, 0, P, 1, 16, 16, 128, P, 0, 16, None) == EALIGN
+    assert g(P, 0, P, 1, P, 0, P, 1, 0, 16, 128, P, 0, 16, None) == OK        # M = 0
+    gg = L.mxq_grouped_scaled_gemm
+    assert gg(P, 0, P, 2, P, 0, P, 1, None, 4, 64, 128, 128, P, 1, None) == ENULL
+    assert gg(P, 0, P, 2, P, 0, P, 1, P, 5000, 64, 128, 128, P, 1, None) == ESHAPE
+    assert gg(P, 0, P, 2, P, 0, P, 1, P, 0, 64, 128, 128, P, 1, None) == OK   # no groups
+
+
+def test_signatures_in_binding_match_header(L):
+    """Every declared function's parameter count matches the binding's."""
+    text = open(HEADER).read()
+    for name in declared_functions():
+        m = re.search(name + r"\s*\(([^;]*)\);", text, re.S)
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        fn = getattr(L, name)
+        assert len(fn.argtypes) == len(params), name

@@ -1,0 +1,238 @@
+"""GPU parity on the five workloads at their full sizes.
+
+Quantized codes and scale bytes are compared bit for bit (whole tensors where
+the oracle is fast enough, else regenerated row slabs); GEMM outputs are
+compared on sampled entries, which the oracle computes one by one from its
+own quantization of the same seeded inputs (the GPU codes are first shown to
+be identical to it), against both the 1e-5 criterion and the MFMA bound.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import mxfp4_precision_numerics_amd as mxq
+from mxfp4_precision_numerics_amd import synth
+from gpu_helpers import (check_gemm, dev_bf16, dev_u8, empty_u8, host, mfma_bound, require_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    O.lib()
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def gpu_mx(xd, fmt, rows, cols, row=True, col=False):
+    q_row = s_row = q_col = s_col = None
+    if row:
+        q_row = empty_u8(rows, cols // 2 if fmt == 2 else cols)
+        s_row = empty_u8(rows, cols // 32)
+    if col:
+        q_col = empty_u8(cols, rows)
+        s_col = empty_u8(cols, rows // 32)
+    mxq.quantize_mx(xd, fmt, q_row, s_row, q_col, s_col)
+    return q_row, s_row, q_col, s_col
+
+
+def sample_entries(g, M, N, n=3000):
+    m = np.concatenate([g.integers(0, M, n), np.full(64, M - 1), np.arange(64) % M])
+    k = np.concatenate([g.integers(0, N, n), np.arange(64) % N, np.full(64, N - 1)])
+    return m.astype(np.int64), k.astype(np.int64)
+
+
+def gemm_check(C_dev, A, fa, sA, ma, B, fb, sB, mb, K, m_idx, n_idx, what):
+    C = host(C_dev)
+    if C.dtype == np.uint16:
+        C = (C.astype(np.uint32) << 16).view(np.float32)
+    got = C[m_idx, n_idx].astype(np.float64)
+    ref, absum = O.gemm_entries(A, fa, sA, ma, B, fb, sB, mb, K, m_idx, n_idx)
+    hb = mfma_bound(A, fa, sA, ma, B, fb, sB, mb, K, m_idx, n_idx)
+    ratio = check_gemm(got, ref, absum, what, hw_bound=hb)
+    log(f"{what}: max |err| / (1e-5 sum|a||b|) = {ratio:.3f}")
+    return ratio
+
+
+def test_workload2_mxfp8_forward():
+    """Llama-3-8B MLP up-projection, MXFP8 E4M3 forward: quantize X and W,
+    GEMM M=4096, N=14336, K=4096."""
+    xs, ws = synth.c2_x(), synth.c2_w()
+    x = synth.tensor(xs)
+    w = synth.tensor(ws)
+    log("workload 2: inputs ready")
+    qx, sx, _, _ = gpu_mx(dev_bf16(x), 0, 4096, 4096)
+    qw, sw, _, _ = gpu_mx(dev_bf16(w), 0, 14336, 4096)
+    oqx, osx, _, _ = O.quantize_mx(x, 0)
+    oqw, osw, _, _ = O.quantize_mx(w, 0)
+    assert np.array_equal(host(qx), oqx) and np.array_equal(host(sx), osx)
+    assert np.array_equal(host(qw), oqw) and np.array_equal(host(sw), osw)
+    log("workload 2: codes and scales bit-exact")
+    C = torch.empty((4096, 14336), dtype=torch.float32, device="cuda")
+    mxq.scaled_gemm(qx, 0, sx, 1, qw, 0, sw, 1, 4096, 14336, 4096, C)
+    m, n = sample_entries(np.random.Generator(np.random.PCG64(2)), 4096, 14336)
+    gemm_check(C, oqx, 0, osx, 1, oqw, 0, osw, 1, 4096, m, n, "workload 2 GEMM")
+
+
+def test_workload3_e5m2_backward_delayed():
+    """E5M2 backward with delayed scaling: 16 prior gradient steps fill the
+    amax history; dgrad (K=14336) and wgrad (K=4096 tokens) GEMMs."""
+    hist_g = torch.zeros(16, dtype=torch.float32, device="cuda")
+    hist_o = np.zeros(16, np.float32)
+    amax = torch.empty(1, device="cuda")
+    sc = torch.empty(1, device="cuda")
+    si = torch.empty(1, device="cuda")
+    for t in range(16):
+        p = synth.tensor(synth.c3_prior_dy(t))
+        qd = empty_u8(p.shape[0], p.shape[1])
+        mxq.quantize_per_tensor(dev_bf16(p), 1, amax, sc, si, qd, amax_history=hist_g)
+        O.quantize_per_tensor(p, 1, history=hist_o)
+    assert np.array_equal(host(hist_g), hist_o)
+    log("workload 3: history of 16 prior steps identical")
+    dy = synth.tensor(synth.c3_dy())
+    q_row = empty_u8(4096, 14336)
+    q_col = empty_u8(14336, 4096)
+    mxq.quantize_per_tensor(dev_bf16(dy), 1, amax, sc, si, q_row, q_col, amax_history=hist_g)
+    od = O.quantize_per_tensor(dy, 1, history=hist_o, row=True, col=True)
+    assert np.array_equal(host(q_row), od["q_row"]) and np.array_equal(host(q_col), od["q_col"])
+    assert host(si)[0] == od["scale_inv"] and host(amax)[0] == od["amax"]
+    assert np.array_equal(host(hist_g), hist_o)
+    dy_sinv = od["scale_inv"]
+    log("workload 3: dY E5M2 codes (row and col) bit-exact")
+    # X and W: E4M3, delayed scaling whose history holds the previous step's amax
+    res = {}
+    for name, spec in (("x", synth.c3_x()), ("w", synth.c3_w())):
+        v = synth.tensor(spec)
+        r, c = v.shape
+        hg = torch.zeros(16, dtype=torch.float32, device="cuda")
+        ho = np.zeros(16, np.float32)
+        qr, qc = empty_u8(r, c), empty_u8(c, r)
+        for _ in range(2):
+            mxq.quantize_per_tensor(dev_bf16(v), 0, amax, sc, si, qr, qc, amax_history=hg)
+            o = O.quantize_per_tensor(v, 0, history=ho, row=True, col=True)
+        assert np.array_equal(host(qr), o["q_row"]) and np.array_equal(host(qc), o["q_col"])
+        assert host(si)[0] == o["scale_inv"]
+        res[name] = (qc, o)
+    log("workload 3: X and W E4M3 codes bit-exact")
+    g = np.random.Generator(np.random.PCG64(3))
+    # dgrad: dX[tok, in] = sum_out dY[tok, out] W[out, in]; B = W^T stored [in, out] = W colwise
+    qwc, ow = res["w"]
+    C = torch.empty((4096, 4096), dtype=torch.float32, device="cuda")
+    s_dy = torch.tensor([dy_sinv], device="cuda")
+    s_w = torch.tensor([ow["scale_inv"]], device="cuda")
+    mxq.scaled_gemm(q_row, 1, s_dy, 0, qwc, 0, s_w, 0, 4096, 4096, 14336, C)
+    m, n = sample_entries(g, 4096, 4096)
+    gemm_check(C, od["q_row"], 1, dy_sinv, 0, ow["q_col"], 0, ow["scale_inv"], 0, 14336, m, n, "dgrad")
+    # wgrad: dW^T[in, out] = sum_tok X[tok, in] dY[tok, out]; A = X colwise, B = dY colwise
+    qxc, ox = res["x"]
+    C2 = torch.empty((4096, 14336), dtype=torch.float32, device="cuda")
+    s_x = torch.tensor([ox["scale_inv"]], device="cuda")
+    mxq.scaled_gemm(qxc, 0, s_x, 0, q_col, 1, s_dy, 0, 4096, 14336, 4096, C2)
+    m, n = sample_entries(g, 4096, 14336)
+    gemm_check(C2, ox["q_col"], 0, ox["scale_inv"], 0, od["q_col"], 1, dy_sinv, 0, 4096, m, n, "wgrad")
+
+
+def test_workload4_mxfp4_repack_grouped():
+    """MoE share: BF16 -> MXFP4 quantize of X, routing gather + direct
+    FP4 -> FP8 repack, grouped GEMM over 32 local experts (gate+up, N=4096)."""
+    x = synth.tensor(synth.c4_x())
+    idx, off = synth.c4_routing()
+    R = int(off[-1])
+    log(f"workload 4: R = {R} routed rows")
+    q4, s4, _, _ = gpu_mx(dev_bf16(x), 2, 8192, 7168)
+    oq4, os4, _, _ = O.quantize_mx(x, 2)
+    assert np.array_equal(host(q4), oq4) and np.array_equal(host(s4), os4)
+    log("workload 4: MXFP4 codes bit-exact")
+    q8 = empty_u8(R, 7168)
+    s8 = empty_u8(R, 56)
+    mxq.repack_fp4_to_fp8(q4, s4, q8, s8, gather_idx=torch.from_numpy(idx).cuda())
+    oq8, os8 = O.repack_fp4_to_fp8(oq4, os4, idx=idx)
+    assert np.array_equal(host(q8), oq8) and np.array_equal(host(s8), os8)
+    log("workload 4: repacked FP8 bit-exact")
+    del x
+    qw = empty_u8(32, 4096, 7168)
+    sw = empty_u8(32, 4096, 224)
+    oqw = np.empty((32, 4096, 7168), np.uint8)
+    osw = np.empty((32, 4096, 224), np.uint8)
+    for e in range(32):
+        w = synth.tensor(synth.c4_w(e))
+        mxq.quantize_mx(dev_bf16(w), 0, qw[e], sw[e])
+        oqw[e], osw[e], _, _ = O.quantize_mx(w, 0)
+    assert np.array_equal(host(qw), oqw) and np.array_equal(host(sw), osw)
+    log("workload 4: expert weights MXFP8 bit-exact")
+    C = torch.empty((R, 4096), dtype=torch.bfloat16, device="cuda")
+    mxq.grouped_scaled_gemm(q8, 0, s8, 2, qw, 0, sw, 1, torch.from_numpy(off).cuda(), 32, R, 4096, 7168, C,
+                            out=mxq.OUT_BF16)
+    g = np.random.Generator(np.random.PCG64(4))
+    m, n = sample_entries(g, R, 4096, 2000)
+    got = (host(C).astype(np.uint32) << 16).view(np.float32)[m, n].astype(np.float64)
+    ref, absum = O.grouped_gemm_entries(oq8, 0, os8, 2, oqw, 0, osw, 1, off, 4096, 7168, m, n)
+    grp = np.searchsorted(off, m, side="right") - 1
+    hb = np.empty(len(m))
+    for gi in np.unique(grp):
+        sel = grp == gi
+        hb[sel] = mfma_bound(oq8, 0, os8, 2, oqw[gi], 0, osw[gi], 1, 7168, m[sel], n[sel])
+    # bf16 output: RNE to 8 significant bits on top of the fp32 result
+    err = np.abs(got - ref)
+    assert np.all(err <= 2.0 ** -8 * (np.abs(ref) + hb) + hb)
+    r = float((np.maximum(err - 2.0 ** -8 * np.abs(ref), 0) / (1e-5 * absum)).max())
+    log(f"workload 4 grouped GEMM (bf16 out): max |err - bf16 rounding| / (1e-5 sum) = {r:.3f}")
+
+
+@pytest.mark.slow
+def test_workload5_llama70b_mxfp8():
+    """Llama-3-70B shapes: MXFP8 up-projection GEMM M=8192, N=28672, K=8192 on
+    Student-t(3) activations; dual (row + col) quantization of H.  Codes are
+    checked on regenerated row slabs."""
+    xs, ws, hs = synth.c5_x(), synth.c5_w_up(), synth.c5_h()
+    x = synth.tensor(xs)
+    w = synth.tensor(ws)
+    log("workload 5: X, W_up ready")
+    qx, sx, _, _ = gpu_mx(dev_bf16(x), 0, 8192, 8192)
+    qw, sw, _, _ = gpu_mx(dev_bf16(w), 0, 28672, 8192)
+    del x, w
+    C = torch.empty((8192, 28672), dtype=torch.float32, device="cuda")
+    mxq.scaled_gemm(qx, 0, sx, 1, qw, 0, sw, 1, 8192, 28672, 8192, C)
+    g = np.random.Generator(np.random.PCG64(5))
+    sl_x = [0, 5, synth.n_slabs(xs) - 1]
+    sl_w = [0, 13, synth.n_slabs(ws) - 1]
+    ox = {}
+    ow = {}
+    hqx, hsx, hqw, hsw = host(qx), host(sx), host(qw), host(sw)
+    for j in sl_x:
+        r0, r1 = synth.rows_of_slab(xs, j)
+        ox[j] = O.quantize_mx(synth.slab(xs, j), 0)[:2]
+        assert np.array_equal(hqx[r0:r1], ox[j][0]) and np.array_equal(hsx[r0:r1], ox[j][1])
+    for j in sl_w:
+        r0, r1 = synth.rows_of_slab(ws, j)
+        ow[j] = O.quantize_mx(synth.slab(ws, j), 0)[:2]
+        assert np.array_equal(hqw[r0:r1], ow[j][0]) and np.array_equal(hsw[r0:r1], ow[j][1])
+    log("workload 5: sampled slabs of X, W_up codes bit-exact")
+    Ch = host(C)
+    worst = 0.0
+    for jx in sl_x:
+        for jw in sl_w:
+            mi = g.integers(0, 1024, 300)
+            ni = g.integers(0, 1024, 300)
+            got = Ch[synth.rows_of_slab(xs, jx)[0] + mi, synth.rows_of_slab(ws, jw)[0] + ni].astype(np.float64)
+            ref, absum = O.gemm_entries(ox[jx][0], 0, ox[jx][1], 1, ow[jw][0], 0, ow[jw][1], 1, 8192, mi, ni)
+            hb = mfma_bound(ox[jx][0], 0, ox[jx][1], 1, ow[jw][0], 0, ow[jw][1], 1, 8192, mi, ni)
+            worst = max(worst, check_gemm(got, ref, absum, f"up-proj slabs {jx},{jw}", hw_bound=hb))
+    log(f"workload 5 up-projection GEMM: max |err| / (1e-5 sum|a||b|) = {worst:.3f}")
+    del C, Ch
+    h = synth.tensor(hs)
+    qh, sh, qhc, shc = gpu_mx(dev_bf16(h), 0, 8192, 28672, row=True, col=True)
+    del h
+    hq, hs_, hqc, hsc = host(qh), host(sh), host(qhc), host(shc)
+    for j in (0, 7):
+        r0, r1 = synth.rows_of_slab(hs, j)
+        oq, os_, oqc, osc = O.quantize_mx(synth.slab(hs, j), 0, row=True, col=True)
+        assert np.array_equal(hq[r0:r1], oq) and np.array_equal(hs_[r0:r1], os_)
+        assert np.array_equal(hqc[:, r0:r1], oqc) and np.array_equal(hsc[:, r0 // 32:r1 // 32], osc)
+    log("workload 5: dual (row+col) quantization of H bit-exact on sampled slabs")
