@@ -93,7 +93,7 @@ enum {
  *             Also used as the reduction accumulator (overwritten first).
  *  scale_out  device float[1]: scale = fl32(F_max / amax_ref), F_max = 448
  *             or 57344; 1.0 if amax_ref is 0, Inf or NaN; FLT_MAX if the
- *             quotient overflows.  May be NULL only if scale_inv_out is not.
+ *             quotient overflows.  Required.
  *  scale_inv_out device float[1]: fl32(1 / scale) (the dequant factor the
  *             GEMM takes as MXQ_SCALE_TENSOR).  May be NULL.
  *  q_row      [rows, cols] codes q = cast(fl32(x * scale)), or NULL
@@ -168,7 +168,8 @@ int mxq_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const int32_t* g
  * fp32 result in the epilogue.  Any mix of E4M3/E5M2/E2M1 operands and scale
  * modes is accepted.
  * Rules: K % 128 == 0 (a multiple of the K step); M, N >= 0; ldc >= N with
- * 16-byte aligned row pitch.
+ * 16-byte aligned row pitch; A, B and each block-scale array below 4 GiB
+ * (else MXQ_ERR_SHAPE).
  */
 int mxq_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, const uint8_t* B, int fb,
                     const void* sB, int mb, int64_t M, int64_t N, int64_t K, void* C, int out, int64_t ldc,
@@ -188,7 +189,9 @@ int mxq_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, const uint
  *             past off[G] are not written.  Offsets are read on the device
  *             only (no host synchronisation).
  *  C          [total_rows, N] contiguous, fp32 or bf16
- * Rules: as mxq_scaled_gemm; G <= 4096.
+ * Rules: as mxq_scaled_gemm (the 4 GiB limit applies to A and to each
+ * group's B); G <= 4096.  Rows beyond total_rows are never read, whatever
+ * the offsets say.
  */
 int mxq_grouped_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, const uint8_t* B, int fb,
                             const void* sB, int mb, const int64_t* group_off, int64_t G, int64_t total_rows,

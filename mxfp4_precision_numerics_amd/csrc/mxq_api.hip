@@ -98,6 +98,15 @@ int mxq_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const int32_t* g
                                                     as_stream(stream)));
 }
 
+// The GEMM kernel addresses each operand (per group) and its scale array
+// with 32-bit byte offsets.
+static bool below_4gib(int64_t rows, int64_t K, int fmt, int mode) {
+    const int64_t lim = (int64_t)1 << 32;
+    const int64_t ld = fmt == MXQ_E2M1 ? K / 2 : K;
+    if (rows > 0 && ld > (lim - 1) / rows) return false;
+    return mode == MXQ_SCALE_TENSOR || rows * (K / 32) < lim;
+}
+
 static int check_operands(const uint8_t* A, int fa, const void* sA, int ma, const uint8_t* B, int fb,
                           const void* sB, int mb, int64_t K, void* C, int out) {
     if (!valid_fmt(fa) || !valid_fmt(fb) || !valid_mode(ma) || !valid_mode(mb)) return MXQ_ERR_FORMAT;
@@ -118,6 +127,7 @@ int mxq_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, const uint
     if ((ldc * (out == MXQ_OUT_F32 ? 4 : 2)) % 16 != 0) return MXQ_ERR_ALIGN;
     if (M == 0 || N == 0) return MXQ_OK;
     if (((M + 127) / 128) * ((N + 127) / 128) > MAX_GRID_X) return MXQ_ERR_SHAPE;
+    if (!below_4gib(M, K, fa, ma) || !below_4gib(N, K, fb, mb)) return MXQ_ERR_SHAPE;
     mxq::GemmArgs a{};
     a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C;
     a.group_off = nullptr; a.G = 0;
@@ -137,6 +147,7 @@ int mxq_grouped_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, co
     if ((N * (out == MXQ_OUT_F32 ? 4 : 2)) % 16 != 0) return MXQ_ERR_ALIGN;
     if (G == 0 || total_rows == 0 || N == 0) return MXQ_OK;
     if (((total_rows + 127) / 128 + G) * ((N + 127) / 128) > MAX_GRID_X) return MXQ_ERR_SHAPE;
+    if (!below_4gib(total_rows, K, fa, ma) || !below_4gib(N, K, fb, mb)) return MXQ_ERR_SHAPE;
     mxq::GemmArgs a{};
     a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C;
     a.group_off = group_off; a.G = G;

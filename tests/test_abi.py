@@ -107,10 +107,14 @@ def test_gemm_validation(L):
     assert g(P, 0, P, 1, P, 0, P, 1, 16, 18, 128, P, 0, 18, None) == EALIGN   # ldc*4 % 16
     assert g(P + 4, 0, P, 1, P, 0, P, 1, 16, 16, 128, P, 0, 16, None) == EALIGN
     assert g(P, 0, P, 1, P, 0, P, 1, 0, 16, 128, P, 0, 16, None) == OK        # M = 0
+    # operands addressed with 32-bit offsets: 2^25 rows x 128 bytes is 4 GiB
+    assert g(P, 0, P, 0, P, 0, P, 0, 1 << 25, 16, 128, P, 0, 16, None) == ESHAPE
+    assert g(P, 0, P, 0, P, 2, P, 0, 16, 1 << 26, 128, P, 0, 1 << 26, None) == ESHAPE  # E2M1 B: 4 GiB
     gg = L.mxq_grouped_scaled_gemm
     assert gg(P, 0, P, 2, P, 0, P, 1, None, 4, 64, 128, 128, P, 1, None) == ENULL
     assert gg(P, 0, P, 2, P, 0, P, 1, P, 5000, 64, 128, 128, P, 1, None) == ESHAPE
     assert gg(P, 0, P, 2, P, 0, P, 1, P, 0, 64, 128, 128, P, 1, None) == OK   # no groups
+    assert gg(P, 0, P, 0, P, 0, P, 0, P, 4, 1 << 25, 128, 128, P, 1, None) == ESHAPE  # A 4 GiB
 
 
 def test_signatures_in_binding_match_header(L):
