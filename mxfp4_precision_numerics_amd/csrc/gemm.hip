@@ -1,5 +1,5 @@
 // gemm.hip - FP8 / MX block-scaled GEMM (dense and ragged grouped) on
-// gfx950's v_mfma_scale_f32_16x16x128_f8f6f4, fp32 accumulation.
+// gfx950's v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation.
 //
 // MoE FP4 page, "Metodologia": the heavy matrix products stay in FP8 on the
 // matrix units; "Kernels CUDA Otimizados": ragged per-expert token counts.
@@ -18,6 +18,20 @@
 // of byte i.  Accumulator lane l, register r is row 8 * (r / 4) + 4 * g +
 // r % 4, column l % 32.  The instruction's op_sel picks which byte of the
 // 32-bit scale operand is used.
+//
+// Pipeline.  K runs in halves of 64 elements (one MFMA deep).  A block
+// (4 waves, 2 x 2 over the tile) keeps a ring of four LDS slots, one K half
+// of the A and B tiles each, and two slots of scale dwords (one per K step of
+// 128).  In half j every wave, after one barrier:
+//   * runs the half's MFMAs from fragments already in registers,
+//   * reads the next half's fragments (slot j+1, landed) into the other
+//     register set, interleaved with the MFMAs,
+//   * starts the global->LDS copy of half j+3 into the slot read in half j-2.
+// So copies get two halves to land and LDS reads one half, both hidden
+// behind MFMAs.  The copies are buffer_load ... lds instructions issued from
+// inline assembly: the compiler's wait insertion cannot see them and so
+// adds no conservative waits; the kernel waits for them explicitly (vmcnt)
+// before the barrier that publishes a slot.
 #include <utility>
 
 #include "common.h"
@@ -25,21 +39,21 @@
 
 namespace mxq {
 
-constexpr int BK = 128;  // K step in elements
 constexpr int NT = 256;  // 4 waves in a 2 x 2 grid, each owning a (BM/2) x (BN/2) sub-tile
 
 template <int F> struct OpInfo {
-    static constexpr int kb = (F == E2M1) ? 64 : 128;  // bytes per row per K step
-    static constexpr int chunks = kb / 16;              // 16-byte chunks per row per step
+    static constexpr int kh = (F == E2M1) ? 32 : 64;  // bytes per row per K half
+    static constexpr int chunks = kh / 16;             // 16-byte chunks per row per half
     static constexpr int code = FmtInfo<F>::mfma_code;
 };
 
-// LDS byte offset of 16-byte chunk `c` of tile row `r` (XOR swizzle so the
-// fragment reads of consecutive rows hit distinct bank groups).
+// LDS byte offset of 16-byte chunk `c` of row `r` within one half-slot (XOR
+// swizzle so that the fragment reads of 8 consecutive rows hit distinct
+// 16-byte bank groups).
 template <int F> __device__ __forceinline__ int lds_off(int r, int c) {
     constexpr int CH = OpInfo<F>::chunks;
-    const int sw = (CH == 8) ? (r & 7) : ((r >> 1) & 3);
-    return r * OpInfo<F>::kb + ((c ^ sw) << 4);
+    const int sw = (CH == 4) ? ((r >> 1) & 3) : ((r >> 2) & 1);
+    return r * OpInfo<F>::kh + ((c ^ sw) << 4);
 }
 
 struct Tile {
@@ -101,90 +115,97 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Raw buffer resource over `bytes` bytes at `p` (gfx9 data format word;
-// reads at or past `bytes` return zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// A block-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Raw buffer resource over `bytes` bytes at `p` (stride 0, gfx9 data format
+// word; loads at or past `bytes` return zero).
+__device__ __forceinline__ v4u make_rsrc(const void* p, int64_t bytes) {
+    const uint64_t a = (uint64_t)p;
+    return v4u{(unsigned)a, (unsigned)(a >> 32) & 0xFFFFu, (unsigned)(uint32_t)bytes, 0x00020000u};
+}
 
-// Global -> LDS copy of one operand tile for K step ks, straight into LDS
-// (buffer_load_dwordx4 ... lds: lane L of a wave fills bytes 16L..16L+15 of
-// the wave's 1 KiB destination).  Buffer loads are counted by vmcnt alone,
-// so LDS reads issued before them can still be waited for one by one.  Each
-// lane picks the global chunk that belongs at its LDS slot, so the LDS image
-// carries the XOR swizzle of lds_off().  Rows at or past `row_end` read the
-// last valid row instead: they only feed output rows (or columns) that are
-// never stored.  The per-lane offset is fixed; the K step enters as the
-// wave-uniform offset (operands stay below 4 GiB).
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (LDS and export counters not waited for).
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// 32-bit LDS address of a __shared__ object (what M0 takes below).
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+// Global -> LDS copies: lane L writes bytes [size*L, size*(L+1)) at the
+// wave-uniform LDS address `dst`, from buffer offset voff + soff.
+__device__ __forceinline__ void dma16(const v4u& rsrc, uint32_t voff, uint32_t soff, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                 ::"v"(voff), "s"(rsrc), "s"(dst), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const v4u& rsrc, uint32_t voff, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, 0 offen lds"
+                 ::"v"(voff), "s"(dst), "s"(rsrc) : "memory", "m0");
+}
+
+// One K half of an operand tile into a half-slot: each wave copies PER_WAVE
+// 1 KiB pieces (piece i of wave w covers tile rows (w + 4i) * RP ...); lane
+// L's position holds the global chunk that belongs there under the lds_off()
+// swizzle, which is the same for every piece.  Rows past the operand's end
+// (a partial last tile) fall outside the buffer's range and read zero; in a
+// grouped operand they read the next group's rows.  Either way they only feed
+// outputs that are never stored.  The per-lane offset of piece 0 is kept;
+// piece i adds i * RP * 4 rows, the K half enters as the uniform offset
+// (operands stay below 4 GiB).
 template <int F, int ROWS>
 struct TileLoader {
-    static constexpr int KB = OpInfo<F>::kb, CH = OpInfo<F>::chunks;
-    static constexpr int NCHUNK = ROWS * KB / 1024;  // 1 KiB pieces per tile
-    static constexpr int PER_WAVE = NCHUNK / 4;
-    static_assert(NCHUNK % 4 == 0, "tile must split over 4 waves");
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t off[PER_WAVE];  // per-lane byte offset of its chunk within the operand at K step 0
-    __device__ __forceinline__ void init(const uint8_t* base, int64_t bytes, int64_t ld, int64_t row0,
-                                         int64_t row_end, int wave, int lane) {
+    static constexpr int KH = OpInfo<F>::kh, CH = OpInfo<F>::chunks;
+    static constexpr int PER_WAVE = ROWS * KH / 1024 / 4;
+    static constexpr int RP = 1024 / KH;  // rows per 1 KiB piece
+    static_assert(PER_WAVE >= 1 && ROWS * KH % 4096 == 0, "tile half must split over 4 waves");
+    v4u rsrc;
+    uint32_t off0, step;  // lane offset of piece 0; bytes between pieces
+    __device__ __forceinline__ void init(const uint8_t* base, int64_t bytes, int64_t ld, int64_t row0, int wave,
+                                         int lane) {
         rsrc = make_rsrc(base, bytes);
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            const int cid = wave + 4 * i;
-            const int o = cid * 1024 + lane * 16;
-            const int r = o / KB, p = (o % KB) / 16;
-            const int sw = (CH == 8) ? (r & 7) : ((r >> 1) & 3);
-            int64_t row = row0 + r;
-            row = row < row_end ? row : row_end - 1;
-            off[i] = (uint32_t)(row * ld + ((p ^ sw) << 4));
-        }
+        const int o = wave * 1024 + lane * 16;
+        const int r = o / KH, p = (o % KH) / 16;
+        const int sw = (CH == 4) ? ((r >> 1) & 3) : ((r >> 2) & 1);
+        off0 = (uint32_t)((row0 + r) * ld + ((p ^ sw) << 4));
+        step = (uint32_t)(4 * RP * ld);
     }
-    __device__ __forceinline__ void issue(int64_t ks, uint8_t* lds_tile, int wave) const {
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_tile + (wave + 4 * i) * 1024), 16,
-                                                     (int)off[i], (int)(uint32_t)(ks * KB), 0, 0);
+    __device__ __forceinline__ void issue(int i, int64_t half, uint32_t slot, int wave) const {
+        dma16(rsrc, off0 + (uint32_t)i * step, (uint32_t)(half * KH), slot + (uint32_t)(wave + 4 * i) * 1024u);
     }
 };
 
-// Global -> LDS copy of one scale dword per tile row for K step ks
-// (buffer_load_dword ... lds: lane L fills bytes 4L..4L+3).  BLK32: the four
-// E8M0 bytes of the step's four 32-blocks (4-aligned because K % 128 == 0).
-// BLK128: the aligned dword that contains the step's byte; the reader picks
-// byte (row * pitch + ks) % 4.  Per-tensor operands load a dword that is
-// never used, so that every mode runs the same straight-line step.
+// One scale dword per tile row for a K step of 128 (one copy per wave).
+// BLK32: the four E8M0 bytes of the step's four 32-blocks (4-aligned since
+// K % 128 == 0).  BLK128: the aligned dword that contains the step's byte;
+// the reader picks byte (row * pitch + ks) % 4.  Per-tensor operands load the
+// dword at offset 0 of their float and never use it, so that every mode runs
+// the same code.  With 128 rows, waves w and w+2 copy the same rows.  Rows
+// past the end read zero or the next group's scales, as for the tiles.
 template <int ROWS>
 struct ScaleLoader {
-    static constexpr int NLOAD = ROWS / 64;  // 64 rows per wave load
-    static_assert(NLOAD % 4 == 0 || NLOAD == 2, "scale rows per wave");
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t off[(NLOAD + 3) / 4];
-    uint32_t kmul;  // bytes per K step: 4 (BLK32), 1 (BLK128), 0 (per-tensor)
-    uint32_t mask;  // ~3 for BLK128 (aligned dword), else ~0
-    __device__ __forceinline__ void init(int mode, const void* s, int64_t K, int64_t rows, int64_t row0,
-                                         int64_t row_end, int wave, int lane) {
+    static_assert(ROWS == 128 || ROWS == 256, "scale rows");
+    v4u rsrc;
+    uint32_t off, kmul, mask;
+    int dst;  // byte offset of this wave's 64 dwords within the scale slot
+    __device__ __forceinline__ void init(int mode, const void* s, int64_t K, int64_t rows, int64_t row0, int wave,
+                                         int lane) {
         const int64_t pitch = (mode == 1) ? K / 32 : (mode == 2 ? K / 128 : 0);
         kmul = mode == 1 ? 4u : (mode == 2 ? 1u : 0u);
         mask = mode == 2 ? ~3u : ~0u;
-        // a per-tensor operand has a 4-byte float behind `s`: offset 0 is valid
         rsrc = make_rsrc(s, mode == 0 ? 4 : rows * pitch);
-#pragma unroll
-        for (int i = 0; i < (NLOAD + 3) / 4; ++i) {
-            int64_t row = row0 + (wave + 4 * i) * 64 + lane;
-            row = row < row_end ? row : row_end - 1;
-            off[i] = (uint32_t)(row * pitch);
-        }
+        const int r = (wave * 64) % ROWS;
+        dst = r * 4;
+        off = (uint32_t)((row0 + r + lane) * pitch);
     }
-    __device__ __forceinline__ void issue(int64_t ks, uint8_t* lds_s, int wave) const {
-#pragma unroll
-        for (int i = 0; i < (NLOAD + 3) / 4; ++i) {
-            if (NLOAD % 4 == 0 || wave + 4 * i < NLOAD) {
-                const uint32_t o = (off[i] + (uint32_t)ks * kmul) & mask;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds_s + (wave + 4 * i) * 256), 4,
-                                                         (int)o, 0, 0, 0);
-            }
-        }
+    __device__ __forceinline__ void issue(int64_t ks, uint32_t slot) const {
+        dma4(rsrc, (off + (uint32_t)ks * kmul) & mask, slot + (uint32_t)dst);
     }
 };
 
@@ -192,60 +213,54 @@ template <int FA, int FB, int BM, int BN>
 __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     using IA = OpInfo<FA>;
     using IB = OpInfo<FB>;
-    constexpr int A_BYTES = BM * IA::kb, B_BYTES = BN * IB::kb;
-    constexpr int STAGE = A_BYTES + B_BYTES + 4 * (BM + BN);  // tiles + scale dwords
-    constexpr int FM = BM / 64, FN = BN / 64;                  // 32-row fragments per wave
-    constexpr int WN = BN / 2;                                 // columns of a wave's sub-tile
-    constexpr int EPI = 4 * 32 * WN * 4;                       // epilogue bands, fp32
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE > EPI ? 2 * STAGE : EPI];  // two stages
+    constexpr int A_H = BM * IA::kh, B_H = BN * IB::kh;  // bytes of one K half of each tile
+    constexpr int SLOT = A_H + B_H;
+    constexpr int SCB = 4 * (BM + BN);                     // scale dwords of one K step
+    constexpr int FM = BM / 64, FN = BN / 64;              // 32-row fragments per wave
+    constexpr int WN = BN / 2;                             // columns of a wave's sub-tile
+    constexpr int NM = FM * FN;                            // MFMAs per half
+    // separate arrays, so the slots are distinct objects to the compiler
+    __shared__ __attribute__((aligned(16))) uint8_t s0[SLOT], s1[SLOT], s2[SLOT], s3[SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t c0[SCB], c1[SCB];
 
     Tile t;
     if (!tile_of_block<BM, BN>(g, t)) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the tile is the same for the whole block: keep it in scalar registers
+    t.m0 = uni64(t.m0);
+    t.m_end = uni64(t.m_end);
+    t.n0 = uni64(t.n0);
+    t.B = (const uint8_t*)uni64((int64_t)t.B);
+    t.sB = (const uint8_t*)uni64((int64_t)t.sB);
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index in a scalar register: LDS copy destinations stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t lda = (FA == E2M1) ? g.K / 2 : g.K;  // bytes per row
     const int64_t ldb = (FB == E2M1) ? g.K / 2 : g.K;
-    const int64_t nks = g.K / BK;
-    const int gq = lane >> 5;  // K block of the instruction this lane feeds
+    const int64_t nks = g.K / 128, H = 2 * nks;         // K steps, K halves
+    const int gq = lane >> 5;                            // K block of the instruction this lane feeds
     const int64_t pA = g.ma == 1 ? g.K / 32 : g.K / 128;  // scale pitch of the operand rows
     const int64_t pB = g.mb == 1 ? g.K / 32 : g.K / 128;
-    // this lane's fragment rows, as offsets within the tile
     const int rA = wm * (BM / 2) + (lane & 31), rB = wn * (BN / 2) + (lane & 31);
 
     // operand extents for the buffer resources (validated below 4 GiB); a
     // grouped A has M = total rows, whatever its offsets claim
-    const int64_t a_rows = g.M;
     TileLoader<FA, BM> ldA;
     TileLoader<FB, BN> ldB;
-    ldA.init(g.A, a_rows * lda, lda, t.m0, t.m_end, wave, lane);
-    ldB.init(t.B, g.N * ldb, ldb, t.n0, g.N, wave, lane);
+    ldA.init(g.A, g.M * lda, lda, t.m0, wave, lane);
+    ldB.init(t.B, g.N * ldb, ldb, t.n0, wave, lane);
     ScaleLoader<BM> lsA;
     ScaleLoader<BN> lsB;
-    lsA.init(g.ma, g.sA, g.K, a_rows, t.m0, t.m_end, wave, lane);
-    lsB.init(g.mb, t.sB, g.K, g.N, t.n0, g.N, wave, lane);
-    auto issue = [&](int64_t ks, uint8_t* st) {
-        ldA.issue(ks, st, wave);
-        ldB.issue(ks, st + A_BYTES, wave);
-        lsA.issue(ks, st + A_BYTES + B_BYTES, wave);
-        lsB.issue(ks, st + A_BYTES + B_BYTES + 4 * BM, wave);
-    };
-    // Operand fragment for K half h of the step (64 K elements): rows r..r+31.
-    auto frag = [&](const uint8_t* base, int r, int h, auto info) -> v8i {
-        using I = decltype(info);
-        if constexpr (I::kb == 64) {
-            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<E2M1>(r, 2 * h + gq));
-            return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        } else {
-            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<E4M3>(r, 4 * h + gq));
-            const uint4 y = *reinterpret_cast<const uint4*>(base + lds_off<E4M3>(r, 4 * h + 2 + gq));
-            return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-        }
-    };
-    // Scale operand of a fragment row: the staged dword shifted so that the
-    // byte for K half h sits at byte 2h (BLK32: blocks 2h + gq; BLK128: the
-    // step's byte copied to bytes 0 and 2).  Per-tensor: 127 (x1) everywhere.
-    // The mode is folded into a shift, mask, multiplier and OR value chosen
-    // once, so the per-step code has no branch:
+    lsA.init(g.ma, g.sA, g.K, g.M, t.m0, wave, lane);
+    lsB.init(g.mb, t.sB, g.K, g.N, t.n0, wave, lane);
+    constexpr int TL = TileLoader<FA, BM>::PER_WAVE + TileLoader<FB, BN>::PER_WAVE;  // tile copies per half
+    // copies of half h: TL, plus 2 scale copies when h is even (a new K step)
+    constexpr int CNT_EVEN = TL + 2, CNT_ODD = TL;
+
+    // Scale operand of a fragment row, from the staged dword: the byte for K
+    // half h ends up at byte 2h (BLK32: blocks 2h + gq; BLK128: the step's
+    // byte copied to bytes 0 and 2); per-tensor: 127 (x1) everywhere.  The
+    // mode is folded into a shift, mask, multiplier and OR value chosen once:
     //   s = (((d >> ((sh + 8 ks k) & 31)) & mask) * mul) | orv
     struct SMode { uint32_t k, mask, mul, orv; };
     auto smode = [](int mode) -> SMode {
@@ -254,89 +269,164 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
         return {1u, 0xFFu, 0x10001u, 0u};
     };
     const SMode smA = smode(g.ma), smB = smode(g.mb);
-    uint32_t shA[FM], shB[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-        shA[i] = g.ma == 1 ? 8u * gq : 8u * (uint32_t)(((t.m0 + rA + 32 * i) * pA) & 3);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-        shB[j] = g.mb == 1 ? 8u * gq : 8u * (uint32_t)(((t.n0 + rB + 32 * j) * pB) & 3);
-    auto sreg = [&](const SMode& m, const uint8_t* lds_s, int r, uint32_t sh, int64_t ks) -> uint32_t {
-        const uint32_t d = *reinterpret_cast<const uint32_t*>(lds_s + r * 4);
-        return (((d >> ((sh + 8u * (uint32_t)ks * m.k) & 31u)) & m.mask) * m.mul) | m.orv;
-    };
+    // (row * pitch) % 4 is the same for every fragment row of this lane: rows
+    // differ by multiples of 32
+    const uint32_t shA = g.ma == 1 ? 8u * gq : 8u * (uint32_t)(((t.m0 + rA) * pA) & 3);
+    const uint32_t shB = g.mb == 1 ? 8u * gq : 8u * (uint32_t)(((t.n0 + rB) * pB) & 3);
 
+    // register sets: fragments of two halves, scale operands of two K steps
+    v8i fa[2][FM], fb[2][FN];
+    uint32_t sa[2][FM], sb[2][FN];
     v16f acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-    // One K step from stage `cur`: read the first K half's fragments; run the
-    // first half's MFMAs while the second half's fragments are read; then, with
-    // every read of `cur` issued, start step ks+1 landing in `nxt` (last read
-    // before the previous barrier) and run the second half's MFMAs.  No LDS
-    // read is ever ordered after an outstanding LDS-bound load.
-    auto step = [&](int64_t ks, const uint8_t* cur, uint8_t* nxt, auto more) {
-        const uint8_t* la = cur;
-        const uint8_t* lb = cur + A_BYTES;
-        const uint8_t* lsa = cur + A_BYTES + B_BYTES;
-        const uint8_t* lsb = lsa + 4 * BM;
-        uint32_t sa[FM], sb[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) sa[i] = sreg(smA, lsa, rA + 32 * i, shA[i], ks);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) sb[j] = sreg(smB, lsb, rB + 32 * j, shB[j], ks);
-        v8i fa[2][FM], fb[2][FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[0][i] = frag(la, rA + 32 * i, 0, IA{});
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[0][j] = frag(lb, rB + 32 * j, 0, IB{});
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[1][i] = frag(la, rA + 32 * i, 1, IA{});
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[1][j] = frag(lb, rB + 32 * j, 1, IB{});
-        // every read of `cur` is issued: start step ks+1 landing in `nxt` (its
-        // last reads were before the previous barrier), so the loads have the
-        // whole step's MFMAs to land
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (decltype(more)::value) issue(ks + 1, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<FN>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            static_for<FM>([&](auto ic) {
-                constexpr int i = decltype(ic)::value;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], acc[i][j], IA::code,
-                                                                            IB::code, 0, (int)sa[i], 0, (int)sb[j]);
-            });
-        });
-        static_for<FN>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            static_for<FM>([&](auto ic) {
-                constexpr int i = decltype(ic)::value;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fb[1][j], acc[i][j], IA::code,
-                                                                            IB::code, 2, (int)sa[i], 2, (int)sb[j]);
-            });
-        });
-        __builtin_amdgcn_sched_barrier(0);  // the wait below must follow every MFMA of the step
-        __builtin_amdgcn_s_waitcnt(0);      // this thread's LDS-bound loads for step ks+1 have landed
+    auto frag_a = [&](const uint8_t* slot, int i) -> v8i {
+        const uint8_t* base = slot;
+        const int r = rA + 32 * i;
+        if constexpr (FA == E2M1) {
+            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<E2M1>(r, gq));
+            return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        } else {
+            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<FA>(r, gq));
+            const uint4 y = *reinterpret_cast<const uint4*>(base + lds_off<FA>(r, 2 + gq));
+            return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        }
+    };
+    auto frag_b = [&](const uint8_t* slot, int j) -> v8i {
+        const uint8_t* base = slot + A_H;
+        const int r = rB + 32 * j;
+        if constexpr (FB == E2M1) {
+            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<E2M1>(r, gq));
+            return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        } else {
+            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<FB>(r, gq));
+            const uint4 y = *reinterpret_cast<const uint4*>(base + lds_off<FB>(r, 2 + gq));
+            return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        }
+    };
+    auto sreg = [&](const SMode& m, uint32_t d, uint32_t sh, int64_t ks) -> uint32_t {
+        return (((d >> ((sh + 8u * (uint32_t)ks * m.k) & 31u)) & m.mask) * m.mul) | m.orv;
+    };
+
+    // Copies for half h (clamped to the last half: a copy past the end lands
+    // in a slot that is never read again), scale dwords with even halves.
+    auto issue_tile = [&](int i, int64_t h, uint32_t slot) {
+        const int64_t hc = h < H ? h : H - 1;
+        if (i < TileLoader<FA, BM>::PER_WAVE)
+            ldA.issue(i, hc, slot, wave);
+        else
+            ldB.issue(i - TileLoader<FA, BM>::PER_WAVE, hc, slot + (uint32_t)A_H, wave);
+    };
+    auto issue_scales = [&](int64_t ks, uint32_t cs) {
+        const int64_t kc = ks < nks ? ks : nks - 1;
+        lsA.issue(kc, cs);
+        lsB.issue(kc, cs + 4u * BM);
+    };
+
+    // One half j.  P: register set holding half j (j % 2); SP: scale set of
+    // its K step; CUR/NXT/FREE: slots of halves j, j+1 and j+3; RS: whether
+    // half j+1 starts a K step (read its scale dwords from CS into set 1-SP
+    // ... the set of step (j+1)/2); NS: whether half j+3 starts a K step
+    // (copy its scales into CN).
+    auto half = [&](int64_t j, auto P_, auto SP_, auto RS_, auto NS_, const uint8_t* nxt, uint32_t fre,
+                    const uint8_t* cs, uint32_t cn) {
+        constexpr int P = decltype(P_)::value, SP = decltype(SP_)::value;
+        constexpr bool RS = decltype(RS_)::value, NS = decltype(NS_)::value;
+        constexpr int Q = 1 - P;                 // register set being filled
+        constexpr int SQ = RS ? 1 - SP : SP;     // scale set being filled (if RS)
+        // wait for half j+1's copies (issued in half j-2); half j+2's may run on
+        // (j has the parity of P; half j+2 has the parity of j)
+        if constexpr (P == 0)
+            __builtin_amdgcn_s_waitcnt(wait_vm(CNT_EVEN));
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vm(CNT_ODD));
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t da[FM], db[FN];
+        if constexpr (RS) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) da[i] = *reinterpret_cast<const uint32_t*>(cs + (rA + 32 * i) * 4);
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj)
+                db[jj] = *reinterpret_cast<const uint32_t*>(cs + 4 * BM + (rB + 32 * jj) * 4);
+        }
+        static_for<NM>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            constexpr int i = k % FM, jj = k / FM;
+            acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fa[P][i], fb[P][jj], acc[i][jj], IA::code, IB::code, 2 * P, (int)sa[SP][i], 2 * P, (int)sb[SP][jj]);
+            // next half's fragments, one per MFMA while they last
+            if constexpr (k < FM) fa[Q][k] = frag_a(nxt, k);
+            if constexpr (k >= FM && k < FM + FN) fb[Q][k - FM] = frag_b(nxt, k - FM);
+            // copies of half j+3, one every other MFMA, scales last
+            if constexpr (k % 2 == 1 && k / 2 < TL) issue_tile(k / 2, j + 3, fre);
+            if constexpr (NS && k == NM - 1) issue_scales((j + 3) / 2, cn);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // copies that did not fit one per two MFMAs
+        static_for<TL>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i >= NM / 2) issue_tile(i, j + 3, fre);
+        });
+        if constexpr (RS) {
+            const int64_t ks = (j + 1) / 2;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sa[SQ][i] = sreg(smA, da[i], shA, ks);
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) sb[SQ][jj] = sreg(smB, db[jj], shB, ks);
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(0, lds);
-    __builtin_amdgcn_s_waitcnt(0);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using BT = std::true_type;
+    using BF = std::false_type;
+
+    // prologue: halves 0, 1, 2 in flight; half 0 and step 0's scales read
+    const uint32_t L0 = lds_addr(s0), L1 = lds_addr(s1), L2 = lds_addr(s2), L3 = lds_addr(s3);
+    const uint32_t LC0 = lds_addr(c0), LC1 = lds_addr(c1);
+    issue_scales(0, LC0);
+    static_for<TL>([&](auto ic) { issue_tile(decltype(ic)::value, 0, L0); });
+    static_for<TL>([&](auto ic) { issue_tile(decltype(ic)::value, 1, L1); });
+    issue_scales(1, LC1);
+    static_for<TL>([&](auto ic) { issue_tile(decltype(ic)::value, 2, L2); });
+    __builtin_amdgcn_s_waitcnt(wait_vm(CNT_ODD + CNT_EVEN));
     __syncthreads();
-    for (int64_t ks = 0; ks + 1 < nks; ++ks) {
-        const int cur = (int)(ks & 1);
-        step(ks, lds + cur * STAGE, lds + (cur ^ 1) * STAGE, std::true_type{});
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        fa[0][i] = frag_a(s0, i);
+        sa[0][i] = sreg(smA, *reinterpret_cast<const uint32_t*>(c0 + (rA + 32 * i) * 4), shA, 0);
     }
-    step(nks - 1, lds + ((nks - 1) & 1) * STAGE, lds, std::false_type{});
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) {
+        fb[0][jj] = frag_b(s0, jj);
+        sb[0][jj] = sreg(smB, *reinterpret_cast<const uint32_t*>(c0 + 4 * BM + (rB + 32 * jj) * 4), shB, 0);
+    }
+
+    // halves in groups of four (two K steps): slots and register sets are
+    // fixed per position in the group
+    int64_t j = 0;
+    for (; j + 4 <= H; j += 4) {
+        half(j + 0, I0{}, I0{}, BF{}, BF{}, s1, L3, c1, LC0);
+        half(j + 1, I1{}, I0{}, BT{}, BT{}, s2, L0, c1, LC0);
+        half(j + 2, I0{}, I1{}, BF{}, BF{}, s3, L1, c0, LC1);
+        half(j + 3, I1{}, I1{}, BT{}, BT{}, s0, L2, c0, LC1);
+    }
+    if (j < H) {  // an odd number of K steps leaves two halves
+        half(j + 0, I0{}, I0{}, BF{}, BF{}, s1, L3, c1, LC0);
+        half(j + 1, I1{}, I0{}, BT{}, BT{}, s2, L0, c1, LC0);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // every copy has landed before the slots are reused
+    __syncthreads();
 
     // Epilogue: per-tensor factors, then fp32 or bf16 (round to nearest even).
-    // Each wave stages one 32-row band of its sub-tile at a time in LDS (the
-    // operand stages are free once the loop's last barrier has passed) and
-    // writes it back as whole rows of 16-byte stores.
+    // Each wave stages bands of BR rows of its sub-tile in one slot (free
+    // once the last barrier has passed) and writes them back as whole rows
+    // of 16-byte stores.
     float alpha = 1.0f;
     if (g.ma == 0) alpha *= ((const float*)g.sA)[0];
     if (g.mb == 0) alpha *= ((const float*)g.sB)[0];
@@ -344,50 +434,57 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     // rows and columns of this wave's sub-tile that exist in C
     const int mlim = (int)min(t.m_end - row_base, (int64_t)(BM / 2));
     const int nlim = (int)min(g.N - col_base, (int64_t)WN);
+    uint8_t* const mine = wave == 0 ? s0 : wave == 1 ? s1 : wave == 2 ? s2 : s3;
     auto store_tile = [&](auto tag) {
         using T = decltype(tag);
         constexpr int PER = 16 / (int)sizeof(T);  // elements per 16-byte chunk
         constexpr int CPR = WN / PER;             // chunks per row
         constexpr int RPI = 64 / CPR;             // rows per wave-wide read
-        T* band = reinterpret_cast<T*>(lds + wave * (32 * WN * 4));
+        constexpr int BR = (32 * WN * (int)sizeof(T) <= SLOT) ? 32 : (16 * WN * (int)sizeof(T) <= SLOT ? 16 : 8);
+        static_assert(BR * WN * (int)sizeof(T) <= SLOT && BR % RPI == 0, "epilogue band");
+        constexpr int RB = BR / 2;                // accumulator registers per band (8 rows <-> 4 registers)
+        T* band = reinterpret_cast<T*>(mine);
         T* cw = (T*)g.C + row_base * g.ldc + col_base;
         const int cc = (lane % CPR) * PER;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            __syncthreads();  // the previous band has been read back
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int b = 0; b < 32 / BR; ++b) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float v = acc[i][j][r] * alpha;
-                    T o;
-                    if constexpr (sizeof(T) == 4) {
-                        o = v;
-                    } else {
-                        const uint32_t u = as_uint(v);
-                        const uint32_t rn = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-                        o = (T)(((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : rn);
+                for (int jj = 0; jj < FN; ++jj)
+#pragma unroll
+                    for (int r = RB * b; r < RB * (b + 1); ++r) {
+                        const float v = acc[i][jj][r] * alpha;
+                        T o;
+                        if constexpr (sizeof(T) == 4) {
+                            o = v;
+                        } else {
+                            const uint32_t u = as_uint(v);
+                            const uint32_t rn = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                            o = (T)(((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : rn);
+                        }
+                        band[(8 * (r / 4) + 4 * gq + (r % 4) - BR * b) * WN + 32 * jj + (lane & 31)] = o;
                     }
-                    band[(8 * (r / 4) + 4 * gq + (r % 4)) * WN + 32 * j + (lane & 31)] = o;
-                }
-            __syncthreads();
+                __syncthreads();
 #pragma unroll
-            for (int q = 0; q < 32 / RPI; ++q) {
-                const int rr = 32 * i + q * RPI + lane / CPR;
-                const uint4 d = *reinterpret_cast<const uint4*>(band + (q * RPI + lane / CPR) * WN + cc);
-                if (rr < mlim) {
-                    T* dst = cw + (int64_t)rr * g.ldc + cc;
-                    if (cc + PER <= nlim) {
-                        *reinterpret_cast<uint4*>(dst) = d;
-                    } else {
-                        const T* e = reinterpret_cast<const T*>(&d);
+                for (int q = 0; q < BR / RPI; ++q) {
+                    const int br = q * RPI + lane / CPR;
+                    const int rr = 32 * i + BR * b + br;
+                    const uint4 d = *reinterpret_cast<const uint4*>(band + br * WN + cc);
+                    if (rr < mlim) {
+                        T* dst = cw + (int64_t)rr * g.ldc + cc;
+                        if (cc + PER <= nlim) {
+                            *reinterpret_cast<uint4*>(dst) = d;
+                        } else {
+                            const T* e = reinterpret_cast<const T*>(&d);
 #pragma unroll
-                        for (int k = 0; k < PER; ++k)
-                            if (cc + k < nlim) dst[k] = e[k];
+                            for (int k = 0; k < PER; ++k)
+                                if (cc + k < nlim) dst[k] = e[k];
+                        }
                     }
                 }
+                __syncthreads();
             }
-        }
     };
     if (g.out == 0)
         store_tile(float{});
