@@ -47,13 +47,19 @@ template <int F> struct OpInfo {
     static constexpr int code = FmtInfo<F>::mfma_code;
 };
 
-// LDS byte offset of 16-byte chunk `c` of row `r` within one half-slot (XOR
-// swizzle so that the fragment reads of 8 consecutive rows hit distinct
-// 16-byte bank groups).
-template <int F> __device__ __forceinline__ int lds_off(int r, int c) {
-    constexpr int CH = OpInfo<F>::chunks;
-    const int sw = (CH == 4) ? ((r >> 1) & 3) : ((r >> 2) & 1);
-    return r * OpInfo<F>::kh + ((c ^ sw) << 4);
+// LDS byte offset of 16-byte chunk `c` of row `r` in a slot whose rows hold
+// RB bytes (64: four chunks, 32: two).  gfx950's LDS serves a ds_read_b128
+// 16 lanes per clock from 64 four-byte banks (256 bytes), so 16 consecutive
+// lanes (16 consecutive rows of a fragment) must land on 16 distinct 16-byte
+// bank quads; the XOR swizzle on the row bits above those that already
+// spread it gives each of the 16 rows its own quad (measured: 4 clocks per
+// wave-wide read, against 8 without it).
+template <int RB> __device__ __forceinline__ int swz(int r) {
+    static_assert(RB == 64 || RB == 32, "LDS row bytes");
+    return (RB == 64) ? ((r >> 2) & 3) : ((r >> 3) & 1);
+}
+template <int RB> __device__ __forceinline__ int lds_off(int r, int c) {
+    return r * RB + ((c ^ swz<RB>(r)) << 4);
 }
 
 struct Tile {
@@ -141,59 +147,65 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 }
 // Global -> LDS copies: lane L writes bytes [size*L, size*(L+1)) at the
 // wave-uniform LDS address `dst`, from buffer offset voff + soff.
+// The resource, destination and uniform offset are block-uniform; they are
+// passed through readfirstlane so that they sit in scalar registers even
+// where the compiler cannot prove uniformity (free where it can).
+__device__ __forceinline__ v4u uni(const v4u& r) {
+    return v4u{(unsigned)__builtin_amdgcn_readfirstlane(r[0]), (unsigned)__builtin_amdgcn_readfirstlane(r[1]),
+               (unsigned)__builtin_amdgcn_readfirstlane(r[2]), (unsigned)__builtin_amdgcn_readfirstlane(r[3])};
+}
 __device__ __forceinline__ void dma16(const v4u& rsrc, uint32_t voff, uint32_t soff, uint32_t dst) {
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-                 ::"v"(voff), "s"(rsrc), "s"(dst), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const v4u& rsrc, uint32_t voff, uint32_t dst) {
-    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, 0 offen lds"
-                 ::"v"(voff), "s"(dst), "s"(rsrc) : "memory", "m0");
+                 ::"v"(voff), "s"(uni(rsrc)), "s"(__builtin_amdgcn_readfirstlane(dst)),
+                   "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
 
-// One K half of an operand tile into a half-slot: each wave copies PER_WAVE
-// 1 KiB pieces (piece i of wave w covers tile rows (w + 4i) * RP ...); lane
-// L's position holds the global chunk that belongs there under the lds_off()
-// swizzle, which is the same for every piece.  Rows past the operand's end
-// (a partial last tile) fall outside the buffer's range and read zero; in a
-// grouped operand they read the next group's rows.  Either way they only feed
-// outputs that are never stored.  The per-lane offset of piece 0 is kept;
-// piece i adds i * RP * 4 rows, the K half enters as the uniform offset
-// (operands stay below 4 GiB).
-template <int F, int ROWS>
+
+// One ring unit (RB bytes of K per row) of an operand tile into a slot:
+// each wave copies PER_WAVE 1 KiB pieces (piece i of wave w covers tile rows
+// (w + 4i) * RP ...); lane L's position holds the global chunk that belongs
+// there under the lds_off() swizzle, which is the same for every piece.
+// Rows past the operand's end (a partial last tile) fall outside the
+// buffer's range and read zero; in a grouped operand they read the next
+// group's rows.  Either way they only feed outputs that are never stored.
+// The per-lane offset of piece 0 is kept; piece i adds i * RP * 4 rows, the
+// unit enters as the uniform offset (operands stay below 4 GiB).
+template <int RB, int ROWS>
 struct TileLoader {
-    static constexpr int KH = OpInfo<F>::kh, CH = OpInfo<F>::chunks;
-    static constexpr int PER_WAVE = ROWS * KH / 1024 / 4;
-    static constexpr int RP = 1024 / KH;  // rows per 1 KiB piece
-    static_assert(PER_WAVE >= 1 && ROWS * KH % 4096 == 0, "tile half must split over 4 waves");
+    static constexpr int CH = RB / 16;
+    static constexpr int PER_WAVE = ROWS * RB / 1024 / 4;
+    static constexpr int RP = 1024 / RB;  // rows per 1 KiB piece
+    static_assert(PER_WAVE >= 1 && ROWS * RB % 4096 == 0, "tile unit must split over 4 waves");
     v4u rsrc;
     uint32_t off0, step;  // lane offset of piece 0; bytes between pieces
     __device__ __forceinline__ void init(const uint8_t* base, int64_t bytes, int64_t ld, int64_t row0, int wave,
                                          int lane) {
         rsrc = make_rsrc(base, bytes);
         const int o = wave * 1024 + lane * 16;
-        const int r = o / KH, p = (o % KH) / 16;
-        const int sw = (CH == 4) ? ((r >> 1) & 3) : ((r >> 2) & 1);
-        off0 = (uint32_t)((row0 + r) * ld + ((p ^ sw) << 4));
+        const int r = o / RB, p = (o % RB) / 16;
+        off0 = (uint32_t)((row0 + r) * ld + ((p ^ swz<RB>(r)) << 4));
         step = (uint32_t)(4 * RP * ld);
     }
-    __device__ __forceinline__ void issue(int i, int64_t half, uint32_t slot, int wave) const {
-        dma16(rsrc, off0 + (uint32_t)i * step, (uint32_t)(half * KH), slot + (uint32_t)(wave + 4 * i) * 1024u);
+    __device__ __forceinline__ void issue(int i, int64_t unit, uint32_t slot, int wave) const {
+        dma16(rsrc, off0 + (uint32_t)i * step, (uint32_t)(unit * RB), slot + (uint32_t)(wave + 4 * i) * 1024u);
     }
 };
 
-// One scale dword per tile row for a K step of 128 (one copy per wave).
-// BLK32: the four E8M0 bytes of the step's four 32-blocks (4-aligned since
-// K % 128 == 0).  BLK128: the aligned dword that contains the step's byte;
-// the reader picks byte (row * pitch + ks) % 4.  Per-tensor operands load the
-// dword at offset 0 of their float and never use it, so that every mode runs
-// the same code.  With 128 rows, waves w and w+2 copy the same rows.  Rows
-// past the end read zero or the next group's scales, as for the tiles.
+// Scale bytes of a group of SG = 4 K steps, 16 bytes per tile row (one copy
+// per wave).  BLK32: the row's 16 E8M0 bytes of the group's 16 32-blocks
+// (4-aligned since K % 128 == 0).  BLK128: the 16 bytes from the aligned
+// dword that holds the group's first byte, which covers the group's 4 bytes.
+// Per-tensor operands load from offset 0 of their float and never use the
+// data, so that every mode runs the same code.  With 128 rows, waves w and
+// w+2 copy the same rows.  Rows past the end read zero or the next group's
+// scales, as for the tiles (the buffer range check works per dword).
+constexpr int SG = 4;
 template <int ROWS>
 struct ScaleLoader {
     static_assert(ROWS == 128 || ROWS == 256, "scale rows");
     v4u rsrc;
     uint32_t off, kmul, mask;
-    int dst;  // byte offset of this wave's 64 dwords within the scale slot
+    int dst;  // byte offset of this wave's 64 rows within the operand's part of the slot
     __device__ __forceinline__ void init(int mode, const void* s, int64_t K, int64_t rows, int64_t row0, int wave,
                                          int lane) {
         const int64_t pitch = (mode == 1) ? K / 32 : (mode == 2 ? K / 128 : 0);
@@ -201,26 +213,49 @@ struct ScaleLoader {
         mask = mode == 2 ? ~3u : ~0u;
         rsrc = make_rsrc(s, mode == 0 ? 4 : rows * pitch);
         const int r = (wave * 64) % ROWS;
-        dst = r * 4;
+        dst = r * 16;
         off = (uint32_t)((row0 + r + lane) * pitch);
     }
-    __device__ __forceinline__ void issue(int64_t ks, uint32_t slot) const {
-        dma4(rsrc, (off + (uint32_t)ks * kmul) & mask, slot + (uint32_t)dst);
+    __device__ __forceinline__ void issue(int64_t grp, uint32_t slot) const {
+        dma16(rsrc, (off + (uint32_t)(grp * SG) * kmul) & mask, 0u, slot + (uint32_t)dst);
     }
 };
+
+// Copy instructions a wave issues at the last half (position J mod 8) of a
+// ring unit: TL tile copies, plus the 2 scale-group copies at position JS.
+constexpr int copies_at(int J, int TL, int JS) { return TL + ((J % 8 + 8) % 8 == JS ? 2 : 0); }
+// Copies issued at the last halves of the NSL-2 units before the unit that
+// ends at position J (still allowed in flight when that half waits for the
+// next unit's copies); units are SU halves long.
+constexpr int copies_after(int J, int NSL, int SU, int TL, int JS) {
+    int n = 0;
+    for (int d = 1; d <= NSL - 2; ++d) n += copies_at(J - d * SU, TL, JS);
+    return n;
+}
 
 template <int FA, int FB, int BM, int BN>
 __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     using IA = OpInfo<FA>;
     using IB = OpInfo<FB>;
-    constexpr int A_H = BM * IA::kh, B_H = BN * IB::kh;  // bytes of one K half of each tile
+    // Ring unit: SU K halves.  Copies fetch RB contiguous bytes per row; FP4
+    // rows would be only 32 bytes per half, and partial-line copies cost the
+    // CU's address unit about as much as full ones, so FP4 x FP4 stages a
+    // whole K step (64 bytes per row) per unit.
+    constexpr int SU = (FA == E2M1 && FB == E2M1) ? 2 : 1;
+    constexpr int RBA = SU * IA::kh, RBB = SU * IB::kh;  // bytes per row per unit
+    constexpr int A_H = BM * RBA, B_H = BN * RBB;        // bytes of one unit of each tile
     constexpr int SLOT = A_H + B_H;
-    constexpr int SCB = 4 * (BM + BN);                     // scale dwords of one K step
+    constexpr int SCB = 16 * (BM + BN);                    // scale bytes of a group of SG K steps
     constexpr int FM = BM / 64, FN = BN / 64;              // 32-row fragments per wave
     constexpr int WN = BN / 2;                             // columns of a wave's sub-tile
     constexpr int NM = FM * FN;                            // MFMAs per half
+    // ring slots: eight where they fit in LDS, else four (a power of two that
+    // divides the 8 / SU units of the unrolled group of eight halves)
+    constexpr int NSL = (8 * SLOT + 2 * SCB <= 160 * 1024 && SU == 1) ? 8 : 4;
+    constexpr int SLOT_HI = NSL == 8 ? SLOT : 16;
     // separate arrays, so the slots are distinct objects to the compiler
     __shared__ __attribute__((aligned(16))) uint8_t s0[SLOT], s1[SLOT], s2[SLOT], s3[SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t s4[SLOT_HI], s5[SLOT_HI], s6[SLOT_HI], s7[SLOT_HI];
     __shared__ __attribute__((aligned(16))) uint8_t c0[SCB], c1[SCB];
 
     Tile t;
@@ -245,34 +280,41 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
 
     // operand extents for the buffer resources (validated below 4 GiB); a
     // grouped A has M = total rows, whatever its offsets claim
-    TileLoader<FA, BM> ldA;
-    TileLoader<FB, BN> ldB;
+    TileLoader<RBA, BM> ldA;
+    TileLoader<RBB, BN> ldB;
     ldA.init(g.A, g.M * lda, lda, t.m0, wave, lane);
     ldB.init(t.B, g.N * ldb, ldb, t.n0, wave, lane);
     ScaleLoader<BM> lsA;
     ScaleLoader<BN> lsB;
     lsA.init(g.ma, g.sA, g.K, g.M, t.m0, wave, lane);
     lsB.init(g.mb, t.sB, g.K, g.N, t.n0, wave, lane);
-    constexpr int TL = TileLoader<FA, BM>::PER_WAVE + TileLoader<FB, BN>::PER_WAVE;  // tile copies per half
-    // copies of half h: TL, plus 2 scale copies when h is even (a new K step)
-    constexpr int CNT_EVEN = TL + 2, CNT_ODD = TL;
+    constexpr int TLA = TileLoader<RBA, BM>::PER_WAVE;
+    constexpr int TL = TLA + TileLoader<RBB, BN>::PER_WAVE;  // tile copies per unit
 
     // Scale operand of a fragment row, from the staged dword: the byte for K
     // half h ends up at byte 2h (BLK32: blocks 2h + gq; BLK128: the step's
     // byte copied to bytes 0 and 2); per-tensor: 127 (x1) everywhere.  The
-    // mode is folded into a shift, mask, multiplier and OR value chosen once:
-    //   s = (((d >> ((sh + 8 ks k) & 31)) & mask) * mul) | orv
-    struct SMode { uint32_t k, mask, mul, orv; };
-    auto smode = [](int mode) -> SMode {
+    // mode is folded into a shift, two masks and an OR value chosen once
+    // (full-rate shifts and logic only):
+    //   b = (d >> ((sh + 8 ks k) & 31)) & mask;  s = b | ((b << 16) & dup) | orv
+    struct SMode { uint32_t k, mask, dup, orv; };
+    auto smode = [](int mode) __attribute__((always_inline)) -> SMode {
         if (mode == 0) return {0u, 0u, 0u, 0x7F7F7F7Fu};
-        if (mode == 1) return {0u, ~0u, 1u, 0u};
-        return {1u, 0xFFu, 0x10001u, 0u};
+        if (mode == 1) return {0u, ~0u, 0u, 0u};
+        return {1u, 0xFFu, 0xFFFF0000u, 0u};
     };
     const SMode smA = smode(g.ma), smB = smode(g.mb);
     // (row * pitch) % 4 is the same for every fragment row of this lane: rows
     // differ by multiples of 32
-    const uint32_t shA = g.ma == 1 ? 8u * gq : 8u * (uint32_t)(((t.m0 + rA) * pA) & 3);
-    const uint32_t shB = g.mb == 1 ? 8u * gq : 8u * (uint32_t)(((t.n0 + rB) * pB) & 3);
+    const uint32_t rdA = (uint32_t)(((t.m0 + rA) * pA) & 3), rdB = (uint32_t)(((t.n0 + rB) * pB) & 3);
+    const uint32_t shA = g.ma == 1 ? 8u * gq : 8u * rdA;
+    const uint32_t shB = g.mb == 1 ? 8u * gq : 8u * rdB;
+    // byte offset, within a row's 16 staged bytes, of the dword holding step
+    // ks's scale(s): BLK32 dword ks % 4; BLK128 the dword of byte rd + ks % 4
+    const uint32_t kmA = g.ma == 1 ? 4u : 1u, kmB = g.mb == 1 ? 4u : 1u;
+    const uint32_t rdA_ = g.ma == 2 ? rdA : 0u, rdB_ = g.mb == 2 ? rdB : 0u;
+    auto dwA = [&](int64_t ks) __attribute__((always_inline)) -> uint32_t { return ((((uint32_t)ks & 3u) * kmA + rdA_) >> 2) * 4u; };
+    auto dwB = [&](int64_t ks) __attribute__((always_inline)) -> uint32_t { return ((((uint32_t)ks & 3u) * kmB + rdB_) >> 2) * 4u; };
 
     // register sets: fragments of two halves, scale operands of two K steps
     v8i fa[2][FM], fb[2][FN];
@@ -283,143 +325,175 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-    auto frag_a = [&](const uint8_t* slot, int i) -> v8i {
-        const uint8_t* base = slot;
-        const int r = rA + 32 * i;
-        if constexpr (FA == E2M1) {
-            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<E2M1>(r, gq));
+    // Fragment of rows r .. r+31 for K half `sub` of a unit (chunk indexes
+    // within an RB-byte row: FP8 halves are chunks g and 2+g of a 64-byte
+    // row; FP4 half `sub` is chunk 2*sub + g of a 64-byte row, or chunk g of
+    // a 32-byte one).
+    auto frag = [&](const uint8_t* base, int r, int sub, auto info, auto rb) __attribute__((always_inline)) -> v8i {
+        using I = decltype(info);
+        constexpr int RB = decltype(rb)::value;
+        if constexpr (I::kh == 32) {
+            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, 2 * sub + gq));
             return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
         } else {
-            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<FA>(r, gq));
-            const uint4 y = *reinterpret_cast<const uint4*>(base + lds_off<FA>(r, 2 + gq));
+            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, gq));
+            const uint4 y = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, 2 + gq));
             return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
         }
     };
-    auto frag_b = [&](const uint8_t* slot, int j) -> v8i {
-        const uint8_t* base = slot + A_H;
-        const int r = rB + 32 * j;
-        if constexpr (FB == E2M1) {
-            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<E2M1>(r, gq));
-            return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        } else {
-            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<FB>(r, gq));
-            const uint4 y = *reinterpret_cast<const uint4*>(base + lds_off<FB>(r, 2 + gq));
-            return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+    auto frag_a = [&](const uint8_t* slot, int i, int sub) __attribute__((always_inline)) -> v8i {
+        return frag(slot, rA + 32 * i, sub, IA{}, std::integral_constant<int, RBA>{});
+    };
+    auto frag_b = [&](const uint8_t* slot, int j, int sub) __attribute__((always_inline)) -> v8i {
+        return frag(slot + A_H, rB + 32 * j, sub, IB{}, std::integral_constant<int, RBB>{});
+    };
+    // shift of step ks for an operand (the same for all its fragment rows)
+    auto sshift = [&](const SMode& m, uint32_t sh, int64_t ks) __attribute__((always_inline)) -> uint32_t {
+        return (sh + 8u * ((uint32_t)ks & 3u) * m.k) & 31u;
+    };
+    auto sreg = [&](const SMode& m, uint32_t d, uint32_t shift) __attribute__((always_inline)) -> uint32_t {
+        const uint32_t b = (d >> shift) & m.mask;
+        return b | ((b << 16) & m.dup) | m.orv;
+    };
+
+    // slot I of the ring (compile-time I)
+    auto slot = [&](auto I_) __attribute__((always_inline)) -> uint8_t* {
+        constexpr int I = decltype(I_)::value;
+        if constexpr (I == 0) return s0;
+        else if constexpr (I == 1) return s1;
+        else if constexpr (I == 2) return s2;
+        else if constexpr (I == 3) return s3;
+        else if constexpr (I == 4) return s4;
+        else if constexpr (I == 5) return s5;
+        else if constexpr (I == 6) return s6;
+        else return s7;
+    };
+    const uint32_t LC0 = lds_addr(c0), LC1 = lds_addr(c1);
+    const int64_t NU = H / SU;  // ring units
+    // Copies of unit v (clamped to the last unit: a copy past the end lands in
+    // a slot that is never read again).
+    auto issue_tile = [&](int i, int64_t v, uint32_t dst) __attribute__((always_inline)) {
+        const int64_t vc = v < NU ? v : NU - 1;
+        if (i < TLA)
+            ldA.issue(i, vc, dst, wave);
+        else
+            ldB.issue(i - TLA, vc, dst + (uint32_t)A_H, wave);
+    };
+    // Scale group u (K steps 4u .. 4u+3) into scale slot u % 2.
+    auto issue_scales = [&](int64_t grp) __attribute__((always_inline)) {
+        const uint32_t cs = LC0 + (uint32_t)(grp & 1) * (LC1 - LC0);  // (a select here defeats SROA)
+        lsA.issue(grp, cs);
+        lsB.issue(grp, cs + 16u * BM);
+    };
+    // Schedule: unit v (halves SU*v ..) lives in slot v % NSL.  Its copies are
+    // issued in the last half of unit v - NSL, right after that half's
+    // barrier (all reads of the slot are done by then); the prologue issues
+    // units 0 .. NSL-1.  The scale group that starts at half 8u is issued
+    // first, with the copies of the unit holding half 8u; its issuing half
+    // sits at position JS (mod 8):
+    constexpr int JS = ((8 - NSL * SU + SU - 1) % 8 + 8) % 8;
+    static_assert(NSL * TL + 2 <= 63, "copies in flight must fit the vmcnt counter");
+    static_assert((8 / SU) % NSL == 0, "slots must repeat within a group of eight halves");
+
+    // One half j at position J = j % 8 of a group of eight halves (four K
+    // steps): MFMAs of half j from register set j % 2 while the fragments of
+    // half j+1 are read into the other set.  In the last half of a unit the
+    // half waits for the next unit's copies, passes a barrier and refills
+    // the unit's slot with unit + NSL.  At odd positions half j+1 starts a K
+    // step: its scales are read and its scale operands formed.
+    auto half = [&](int64_t j, auto J_) __attribute__((always_inline)) {
+        constexpr int J = decltype(J_)::value;
+        constexpr int P = J & 1, Q = 1 - P;       // register set of half j, of half j+1
+        constexpr int SP = (J >> 1) & 1;          // scale set of half j's K step
+        constexpr bool RS = (J & 1) == 1;         // read the scales of step (j+1)/2
+        constexpr int SQ = ((J + 1) >> 1) & 1;    // their scale set
+        constexpr int SUB = J % SU, SUB1 = (J + 1) % SU;       // halves within units
+        constexpr bool LAST = SUB == SU - 1;      // last half of its unit
+        constexpr int CUR = (J / SU) % NSL, NXT = ((J + 1) / SU) % NSL;
+        uint32_t dst = 0;
+        if constexpr (LAST) {
+            // wait for the next unit's copies; those of the NSL-2 units
+            // issued after them may still run
+            __builtin_amdgcn_s_waitcnt(wait_vm(copies_after(J, NSL, SU, TL, JS)));
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            dst = lds_addr(slot(std::integral_constant<int, CUR>{}));
+            if constexpr (J == JS) issue_scales((j + 1 + (NSL - 1) * SU) / (2 * SG));
         }
-    };
-    auto sreg = [&](const SMode& m, uint32_t d, uint32_t sh, int64_t ks) -> uint32_t {
-        return (((d >> ((sh + 8u * (uint32_t)ks * m.k) & 31u)) & m.mask) * m.mul) | m.orv;
-    };
-
-    // Copies for half h (clamped to the last half: a copy past the end lands
-    // in a slot that is never read again), scale dwords with even halves.
-    auto issue_tile = [&](int i, int64_t h, uint32_t slot) {
-        const int64_t hc = h < H ? h : H - 1;
-        if (i < TileLoader<FA, BM>::PER_WAVE)
-            ldA.issue(i, hc, slot, wave);
-        else
-            ldB.issue(i - TileLoader<FA, BM>::PER_WAVE, hc, slot + (uint32_t)A_H, wave);
-    };
-    auto issue_scales = [&](int64_t ks, uint32_t cs) {
-        const int64_t kc = ks < nks ? ks : nks - 1;
-        lsA.issue(kc, cs);
-        lsB.issue(kc, cs + 4u * BM);
-    };
-
-    // One half j.  P: register set holding half j (j % 2); SP: scale set of
-    // its K step; CUR/NXT/FREE: slots of halves j, j+1 and j+3; RS: whether
-    // half j+1 starts a K step (read its scale dwords from CS into set 1-SP
-    // ... the set of step (j+1)/2); NS: whether half j+3 starts a K step
-    // (copy its scales into CN).
-    auto half = [&](int64_t j, auto P_, auto SP_, auto RS_, auto NS_, const uint8_t* nxt, uint32_t fre,
-                    const uint8_t* cs, uint32_t cn) {
-        constexpr int P = decltype(P_)::value, SP = decltype(SP_)::value;
-        constexpr bool RS = decltype(RS_)::value, NS = decltype(NS_)::value;
-        constexpr int Q = 1 - P;                 // register set being filled
-        constexpr int SQ = RS ? 1 - SP : SP;     // scale set being filled (if RS)
-        // wait for half j+1's copies (issued in half j-2); half j+2's may run on
-        // (j has the parity of P; half j+2 has the parity of j)
-        if constexpr (P == 0)
-            __builtin_amdgcn_s_waitcnt(wait_vm(CNT_EVEN));
-        else
-            __builtin_amdgcn_s_waitcnt(wait_vm(CNT_ODD));
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
         uint32_t da[FM], db[FN];
         if constexpr (RS) {
+            const int64_t ks = (j + 1) / 2;
+            const uint8_t* cs = ((ks / SG) & 1) ? c1 : c0;
+            const uint32_t oa = dwA(ks), ob = dwB(ks);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) da[i] = *reinterpret_cast<const uint32_t*>(cs + (rA + 32 * i) * 4);
+            for (int i = 0; i < FM; ++i) da[i] = *reinterpret_cast<const uint32_t*>(cs + (rA + 32 * i) * 16 + oa);
 #pragma unroll
             for (int jj = 0; jj < FN; ++jj)
-                db[jj] = *reinterpret_cast<const uint32_t*>(cs + 4 * BM + (rB + 32 * jj) * 4);
+                db[jj] = *reinterpret_cast<const uint32_t*>(cs + 16 * BM + (rB + 32 * jj) * 16 + ob);
         }
-        static_for<NM>([&](auto kc) {
+        const uint8_t* nxt = slot(std::integral_constant<int, NXT>{});
+        static_for<NM>([&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
             constexpr int i = k % FM, jj = k / FM;
             acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 fa[P][i], fb[P][jj], acc[i][jj], IA::code, IB::code, 2 * P, (int)sa[SP][i], 2 * P, (int)sb[SP][jj]);
             // next half's fragments, one per MFMA while they last
-            if constexpr (k < FM) fa[Q][k] = frag_a(nxt, k);
-            if constexpr (k >= FM && k < FM + FN) fb[Q][k - FM] = frag_b(nxt, k - FM);
-            // copies of half j+3, one every other MFMA, scales last
-            if constexpr (k % 2 == 1 && k / 2 < TL) issue_tile(k / 2, j + 3, fre);
-            if constexpr (NS && k == NM - 1) issue_scales((j + 3) / 2, cn);
+            if constexpr (k < FM) fa[Q][k] = frag_a(nxt, k, SUB1);
+            if constexpr (k >= FM && k < FM + FN) fb[Q][k - FM] = frag_b(nxt, k - FM, SUB1);
+            // copies of unit + NSL, spread evenly over the half's MFMAs (a copy
+            // waits for the CU's address unit; bursts stall the MFMAs)
+            if constexpr (LAST) {
+                static_for<TL>([&](auto ic) __attribute__((always_inline)) {
+                    constexpr int c = decltype(ic)::value;
+                    if constexpr (TL <= NM) {
+                        if constexpr (k == (2 * c + 1) * NM / (2 * TL)) issue_tile(c, j / SU + NSL, dst);
+                    } else {
+                        if constexpr (k == c * NM / TL) issue_tile(c, j / SU + NSL, dst);
+                    }
+                });
+            }
             __builtin_amdgcn_sched_barrier(0);
-        });
-        // copies that did not fit one per two MFMAs
-        static_for<TL>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            if constexpr (i >= NM / 2) issue_tile(i, j + 3, fre);
         });
         if constexpr (RS) {
             const int64_t ks = (j + 1) / 2;
+            const uint32_t xa = sshift(smA, shA, ks), xb = sshift(smB, shB, ks);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) sa[SQ][i] = sreg(smA, da[i], shA, ks);
+            for (int i = 0; i < FM; ++i) sa[SQ][i] = sreg(smA, da[i], xa);
 #pragma unroll
-            for (int jj = 0; jj < FN; ++jj) sb[SQ][jj] = sreg(smB, db[jj], shB, ks);
+            for (int jj = 0; jj < FN; ++jj) sb[SQ][jj] = sreg(smB, db[jj], xb);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using BT = std::true_type;
-    using BF = std::false_type;
-
-    // prologue: halves 0, 1, 2 in flight; half 0 and step 0's scales read
-    const uint32_t L0 = lds_addr(s0), L1 = lds_addr(s1), L2 = lds_addr(s2), L3 = lds_addr(s3);
-    const uint32_t LC0 = lds_addr(c0), LC1 = lds_addr(c1);
-    issue_scales(0, LC0);
-    static_for<TL>([&](auto ic) { issue_tile(decltype(ic)::value, 0, L0); });
-    static_for<TL>([&](auto ic) { issue_tile(decltype(ic)::value, 1, L1); });
-    issue_scales(1, LC1);
-    static_for<TL>([&](auto ic) { issue_tile(decltype(ic)::value, 2, L2); });
-    __builtin_amdgcn_s_waitcnt(wait_vm(CNT_ODD + CNT_EVEN));
+    // prologue: scale group 0 and units 0 .. NSL-1 in flight; half 0 and
+    // step 0's scales read
+    issue_scales(0);
+    static_for<NSL>([&](auto uc) __attribute__((always_inline)) {
+        const uint32_t dst = lds_addr(slot(uc));
+        static_for<TL>([&](auto ic) __attribute__((always_inline)) {
+            issue_tile(decltype(ic)::value, decltype(uc)::value, dst);
+        });
+    });
+    __builtin_amdgcn_s_waitcnt(wait_vm((NSL - 1) * TL));
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        fa[0][i] = frag_a(s0, i);
-        sa[0][i] = sreg(smA, *reinterpret_cast<const uint32_t*>(c0 + (rA + 32 * i) * 4), shA, 0);
+        fa[0][i] = frag_a(s0, i, 0);
+        sa[0][i] = sreg(smA, *reinterpret_cast<const uint32_t*>(c0 + (rA + 32 * i) * 16 + dwA(0)), sshift(smA, shA, 0));
     }
 #pragma unroll
     for (int jj = 0; jj < FN; ++jj) {
-        fb[0][jj] = frag_b(s0, jj);
-        sb[0][jj] = sreg(smB, *reinterpret_cast<const uint32_t*>(c0 + 4 * BM + (rB + 32 * jj) * 4), shB, 0);
+        fb[0][jj] = frag_b(s0, jj, 0);
+        sb[0][jj] = sreg(smB, *reinterpret_cast<const uint32_t*>(c0 + 16 * BM + (rB + 32 * jj) * 16 + dwB(0)), sshift(smB, shB, 0));
     }
 
-    // halves in groups of four (two K steps): slots and register sets are
-    // fixed per position in the group
+    // groups of eight halves; then the 0, 2, 4 or 6 that remain
     int64_t j = 0;
-    for (; j + 4 <= H; j += 4) {
-        half(j + 0, I0{}, I0{}, BF{}, BF{}, s1, L3, c1, LC0);
-        half(j + 1, I1{}, I0{}, BT{}, BT{}, s2, L0, c1, LC0);
-        half(j + 2, I0{}, I1{}, BF{}, BF{}, s3, L1, c0, LC1);
-        half(j + 3, I1{}, I1{}, BT{}, BT{}, s0, L2, c0, LC1);
-    }
-    if (j < H) {  // an odd number of K steps leaves two halves
-        half(j + 0, I0{}, I0{}, BF{}, BF{}, s1, L3, c1, LC0);
-        half(j + 1, I1{}, I0{}, BT{}, BT{}, s2, L0, c1, LC0);
-    }
+    for (; j + 8 <= H; j += 8)
+        static_for<8>([&](auto Jc) __attribute__((always_inline)) { half(j + decltype(Jc)::value, Jc); });
+    static_for<7>([&](auto Jc) __attribute__((always_inline)) {
+        if (j + decltype(Jc)::value < H) half(j + decltype(Jc)::value, Jc);
+    });
     __builtin_amdgcn_s_waitcnt(wait_vm(0));  // every copy has landed before the slots are reused
     __syncthreads();
 
@@ -435,7 +509,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     const int mlim = (int)min(t.m_end - row_base, (int64_t)(BM / 2));
     const int nlim = (int)min(g.N - col_base, (int64_t)WN);
     uint8_t* const mine = wave == 0 ? s0 : wave == 1 ? s1 : wave == 2 ? s2 : s3;
-    auto store_tile = [&](auto tag) {
+    auto store_tile = [&](auto tag) __attribute__((always_inline)) {
         using T = decltype(tag);
         constexpr int PER = 16 / (int)sizeof(T);  // elements per 16-byte chunk
         constexpr int CPR = WN / PER;             // chunks per row
