@@ -12,8 +12,14 @@ path measured on their own workloads, and the CPU oracle timed on a bounded
 sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows]
-       [--no-cpu-baseline] [--profile-step]
+       [--no-cpu-baseline] [--copy-probe]
+
+roofline.traffic is the GEMM's HBM bytes per launch from the committed
+rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/ (each counter
+scaled by what it reads for a plain copy of known size, --copy-probe), and
+null when the GEMM source has changed since those counters were taken.
 """
+import hashlib
 import argparse
 import json
 import os
@@ -38,7 +44,29 @@ def parse():
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--row-reps", type=int, default=10)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB elementwise copy (reference for the traffic counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_mxfp8_4096x14336x4096_hbm_traffic.txt")
+GEMM_SRC = os.path.join(ROOT, "mxfp4_precision_numerics_amd", "csrc", "gemm.hip")
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, or None
+    if there is none or the kernel source differs from the one counted."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    if kv.get("gemm_source_sha256") != sha or "traffic_bytes" not in kv:
+        return None
+    return int(float(kv["traffic_bytes"]))
 
 
 def main():
@@ -117,9 +145,9 @@ def main():
                 "N(0,0.02) weights)",
         "config": {"workload": "llama3-8b-mlp-up-mxfp8-fwd", "M": M, "N": N, "K": K,
                    "step": "quantize_mx(X) + quantize_mx(W) + scaled_gemm", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "k_gemm<E4M3,E4M3>", "bound": "mfma", "achieved": round(gemm_tflops, 1),
+        "roofline": {"kernel": "k_gemm<E4M3,E4M3,256,256>", "bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": gemm_traffic()},
         "kernels_ms": {"quantize_mx_x": round(qx_ms, 4), "quantize_mx_w": round(qw_ms, 4),
                        "scaled_gemm": round(gemm_ms, 4)},
         "quantize_gbs": {"x": round(qbytes_x / (qx_ms * 1e-3) / 1e9, 1),
@@ -127,6 +155,17 @@ def main():
     }
     del C
     torch.cuda.empty_cache()
+
+    if args.copy_probe:
+        # an elementwise kernel that reads and writes exactly 1 GiB each
+        src = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     if not args.no_rows:
         result["rows"] = measure_rows(torch, mxq, synth, dev, args.row_reps)
@@ -259,29 +298,28 @@ def measure_rows(torch, mxq, synth, dev, reps):
 
 def cpu_baseline(synth):
     """The oracle as it stands, on a bounded sample of the headline workload:
-    MX quantization of 1024 rows of X and 1024 rows of W, then the fp64 GEMM
-    on 64 x 256 entries of C (K=4096).  Reported in the headline unit
-    (GEMM FLOP/s of the sample) with the quantize throughput beside it."""
+    MX E4M3 quantization of all of X [4096, 4096] and W [14336, 4096], then
+    the fp64 GEMM on the 1024 x 1536 entries C[0:1024, 0:1536] (K=4096).
+    Reported in the headline unit (GEMM FLOP/s of the sample) with the
+    quantize throughput beside it."""
     import oracle as O
     O.lib()
-    xs, ws = synth.c2_x(), synth.c2_w()
-    x = synth.slab(xs, 0)
-    w = synth.slab(ws, 0)
-    cores = len(os.sched_getaffinity(0))
+    x = synth.tensor(synth.c2_x())
+    w = synth.tensor(synth.c2_w())
     t0 = time.perf_counter()
     qx, sx, _, _ = O.quantize_mx(x, O.E4M3)
     qw, sw, _, _ = O.quantize_mx(w, O.E4M3)
     t1 = time.perf_counter()
-    m = np.repeat(np.arange(64), 256)
-    n = np.tile(np.arange(256), 64)
+    m = np.repeat(np.arange(1024), 1536)
+    n = np.tile(np.arange(1536), 1024)
     O.gemm_entries(qx, O.E4M3, sx, O.SCALE_BLK32, qw, O.E4M3, sw, O.SCALE_BLK32, 4096, m, n)
     t2 = time.perf_counter()
     q_bytes = (x.size + w.size) * (2 + 1 + 1 / 32)
     gemm_flops = 2.0 * 4096 * len(m)
-    return {"value": round(gemm_flops / (t2 - t1) / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "quantize_gbs": round(q_bytes / (t1 - t0) / 1e9, 4),
-            "sample": "MX E4M3 quantize of X[0:1024] and W[0:1024] rows, fp64 GEMM on 64x256 entries of C "
-                      f"(K=4096); quantize {t1 - t0:.2f} s, GEMM {t2 - t1:.2f} s"}
+    return {"value": round(gemm_flops / (t2 - t1) / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(),
+            "kind": "oracle", "quantize_gbs": round(q_bytes / (t1 - t0) / 1e9, 4),
+            "sample": "MX E4M3 quantize of all of X 4096x4096 and W 14336x4096 (bf16), fp64 GEMM on the "
+                      f"1024x1536 entries C[0:1024, 0:1536] (K=4096); quantize {t1 - t0:.1f} s, GEMM {t2 - t1:.1f} s"}
 
 
 if __name__ == "__main__":

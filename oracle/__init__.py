@@ -33,6 +33,8 @@ def lib():
             from . import build as _b
             _b.build()
         L = ctypes.CDLL(_LIB_PATH)
+        L.or_num_threads.restype = ctypes.c_int
+        L.or_num_threads.argtypes = []
         L.or_value.restype = ctypes.c_double
         L.or_value.argtypes = [_i, ctypes.c_uint]
         L.or_e8m0_value.restype = ctypes.c_double
@@ -264,3 +266,8 @@ def grouped_gemm_entries(A, fa, sA, ma, B, fb, sB, mb, off, N, K, m_idx, n_idx):
                                   len(off) - 1, N, K, _ptr(m_idx), _ptr(n_idx), len(m_idx),
                                   _ptr(c), _ptr(cabs))
     return c, cabs
+
+
+def num_threads():
+    """OpenMP threads the oracle's loops run on."""
+    return int(lib().or_num_threads())

@@ -28,6 +28,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <omp.h>
 
 #define OR_E4M3 0
 #define OR_E5M2 1
@@ -625,3 +626,6 @@ void or_grouped_gemm_entries(const uint8_t* A, int fa, const void* sA, int ma, c
             abs_out[t] = aacc;
     }
 }
+
+/* Threads the OpenMP loops above use (for reporting the oracle's timing). */
+int or_num_threads(void) { return omp_get_max_threads(); }
