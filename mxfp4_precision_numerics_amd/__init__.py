@@ -17,6 +17,7 @@ E4M3, E5M2, E2M1 = 0, 1, 2
 SRC_F32, SRC_BF16 = 0, 1
 SCALE_TENSOR, SCALE_BLK32, SCALE_BLK128 = 0, 1, 2
 OUT_F32, OUT_BF16 = 0, 1
+OUT_PRECISE = 16  # OR into `out`: exact products (see include/mxq.h)
 
 _lib = None
 

@@ -29,7 +29,8 @@ struct GemmArgs {
     int64_t ldc;
     int64_t b_group_stride;  // bytes between consecutive B_g
     int64_t sb_group_stride; // bytes between consecutive sB_g (0 for per-tensor)
-    int fa, fb, ma, mb, out;
+    int fa, fb, ma, mb, out;  // out: 0 fp32, 1 bf16
+    int precise;              // exact products (FP8 x FP8 only; E2M1 x E2M1 is exact natively)
 };
 hipError_t launch_scaled_gemm(const GemmArgs& a, hipStream_t st);
 

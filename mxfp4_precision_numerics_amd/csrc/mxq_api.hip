@@ -110,7 +110,10 @@ static bool below_4gib(int64_t rows, int64_t K, int fmt, int mode) {
 static int check_operands(const uint8_t* A, int fa, const void* sA, int ma, const uint8_t* B, int fb,
                           const void* sB, int mb, int64_t K, void* C, int out) {
     if (!valid_fmt(fa) || !valid_fmt(fb) || !valid_mode(ma) || !valid_mode(mb)) return MXQ_ERR_FORMAT;
-    if (out != MXQ_OUT_F32 && out != MXQ_OUT_BF16) return MXQ_ERR_FORMAT;
+    const int kind = out & ~MXQ_OUT_PRECISE;
+    if (kind != MXQ_OUT_F32 && kind != MXQ_OUT_BF16) return MXQ_ERR_FORMAT;
+    // the precise mode takes FP8 x FP8 (E2M1 x E2M1 is exact natively); mixed FP8 x FP4 is refused
+    if ((out & MXQ_OUT_PRECISE) && ((fa == MXQ_E2M1) != (fb == MXQ_E2M1))) return MXQ_ERR_FORMAT;
     if (!A || !B || !sA || !sB || !C) return MXQ_ERR_NULL;
     if (K <= 0 || K % 128 != 0) return MXQ_ERR_SHAPE;
     if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MXQ_ERR_ALIGN;
@@ -124,7 +127,7 @@ int mxq_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, const uint
     const int st = check_operands(A, fa, sA, ma, B, fb, sB, mb, K, C, out);
     if (st != MXQ_OK) return st;
     if (ldc < N) return MXQ_ERR_SHAPE;
-    if ((ldc * (out == MXQ_OUT_F32 ? 4 : 2)) % 16 != 0) return MXQ_ERR_ALIGN;
+    if ((ldc * ((out & ~MXQ_OUT_PRECISE) == MXQ_OUT_F32 ? 4 : 2)) % 16 != 0) return MXQ_ERR_ALIGN;
     if (M == 0 || N == 0) return MXQ_OK;
     if (((M + 127) / 128) * ((N + 127) / 128) > MAX_GRID_X) return MXQ_ERR_SHAPE;
     if (!below_4gib(M, K, fa, ma) || !below_4gib(N, K, fb, mb)) return MXQ_ERR_SHAPE;
@@ -132,7 +135,8 @@ int mxq_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, const uint
     a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C;
     a.group_off = nullptr; a.G = 0;
     a.M = M; a.N = N; a.K = K; a.ldc = ldc;
-    a.fa = fa; a.fb = fb; a.ma = ma; a.mb = mb; a.out = out;
+    a.fa = fa; a.fb = fb; a.ma = ma; a.mb = mb; a.out = out & ~MXQ_OUT_PRECISE;
+    a.precise = (out & MXQ_OUT_PRECISE) && fa != MXQ_E2M1;
     return hip_status(mxq::launch_scaled_gemm(a, as_stream(stream)));
 }
 
@@ -144,7 +148,7 @@ int mxq_grouped_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, co
     if (st != MXQ_OK) return st;
     if (!group_off) return MXQ_ERR_NULL;
     if (!aligned4(group_off)) return MXQ_ERR_ALIGN;
-    if ((N * (out == MXQ_OUT_F32 ? 4 : 2)) % 16 != 0) return MXQ_ERR_ALIGN;
+    if ((N * ((out & ~MXQ_OUT_PRECISE) == MXQ_OUT_F32 ? 4 : 2)) % 16 != 0) return MXQ_ERR_ALIGN;
     if (G == 0 || total_rows == 0 || N == 0) return MXQ_OK;
     if (((total_rows + 127) / 128 + G) * ((N + 127) / 128) > MAX_GRID_X) return MXQ_ERR_SHAPE;
     if (!below_4gib(total_rows, K, fa, ma) || !below_4gib(N, K, fb, mb)) return MXQ_ERR_SHAPE;
@@ -154,7 +158,8 @@ int mxq_grouped_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, co
     a.M = total_rows; a.N = N; a.K = K; a.ldc = N;
     a.b_group_stride = N * (fb == MXQ_E2M1 ? K / 2 : K);
     a.sb_group_stride = mb == MXQ_SCALE_BLK32 ? N * (K / 32) : (mb == MXQ_SCALE_BLK128 ? N * (K / 128) : 0);
-    a.fa = fa; a.fb = fb; a.ma = ma; a.mb = mb; a.out = out;
+    a.fa = fa; a.fb = fb; a.ma = ma; a.mb = mb; a.out = out & ~MXQ_OUT_PRECISE;
+    a.precise = (out & MXQ_OUT_PRECISE) && fa != MXQ_E2M1;
     return hip_status(mxq::launch_scaled_gemm(a, as_stream(stream)));
 }
 

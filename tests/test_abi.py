@@ -102,6 +102,10 @@ def test_gemm_validation(L):
     assert g(P, 3, P, 1, P, 0, P, 1, 16, 16, 128, P, 0, 16, None) == EFMT
     assert g(P, 0, P, 5, P, 0, P, 1, 16, 16, 128, P, 0, 16, None) == EFMT
     assert g(P, 0, P, 1, P, 0, P, 1, 16, 16, 128, P, 2, 16, None) == EFMT    # out type
+    assert g(P, 0, P, 1, P, 0, P, 1, 16, 16, 128, P, 18, 16, None) == EFMT   # precise | bad type
+    assert g(P, 0, P, 1, P, 2, P, 1, 16, 16, 128, P, 16, 16, None) == EFMT   # precise, FP8 x FP4
+    assert g(P, 0, P, 1, P, 0, P, 1, 0, 16, 128, P, 16, 16, None) == OK      # precise, M = 0
+    assert g(P, 2, P, 1, P, 2, P, 1, 0, 16, 128, P, 17, 16, None) == OK      # precise FP4 x FP4 (exact anyway)
     assert g(P, 0, None, 1, P, 0, P, 1, 16, 16, 128, P, 0, 16, None) == ENULL
     assert g(P, 0, P, 1, P, 0, P, 1, 16, 16, 128, P, 0, 8, None) == ESHAPE    # ldc < N
     assert g(P, 0, P, 1, P, 0, P, 1, 16, 18, 128, P, 0, 18, None) == EALIGN   # ldc*4 % 16

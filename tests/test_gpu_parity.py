@@ -279,7 +279,7 @@ def rand_operand(g, fmt, mode, rows, K, nan_codes=False):
 
 
 def run_gemm(A, fa, sA, ma, B, fb, sB, mb, M, N, K, out=0):
-    C = torch.empty((M, N), dtype=torch.float32 if out == 0 else torch.bfloat16, device="cuda")
+    C = torch.empty((M, N), dtype=torch.bfloat16 if out & mxq.OUT_BF16 else torch.float32, device="cuda")
     mxq.scaled_gemm(dev_u8(A), fa, gemm_scale_arg(sA, ma), ma, dev_u8(B), fb, gemm_scale_arg(sB, mb), mb,
                     M, N, K, C, out=out)
     return host(C)
@@ -415,6 +415,98 @@ def test_grouped_gemm_ragged_with_empty_groups():
                                     int(off[gi + 1] - off[gi]), N, K) for gi in range(G)])
     check_gemm(Ch[:int(off[-1])], c.reshape(-1, N), cabs.reshape(-1, N), "grouped", hw_bound=hb)
     assert np.all(Ch[int(off[-1]):] == 12345.0)
+
+
+# ---------------------------------------------------- GEMM, precise mode
+
+FP8_PAIRS = [(0, 0), (1, 0), (0, 1), (1, 1)]
+
+
+@pytest.mark.parametrize("fa,fb", FP8_PAIRS)
+@pytest.mark.parametrize("ma,mb", [(1, 1), (0, 0), (2, 1), (0, 1)])
+def test_gemm_precise_within_1e5(fa, fb, ma, mb):
+    """MXQ_OUT_PRECISE: the same random codes over each FP8 format's whole
+    range, now held to 1e-5 of the fp64 oracle (elementwise and normwise)."""
+    g = np.random.Generator(np.random.PCG64(1600 + fa * 10 + fb + ma * 100 + mb * 1000))
+    M, N, K = 160, 200, 384
+    A, sA = rand_operand(g, fa, ma, M, K)
+    B, sB = rand_operand(g, fb, mb, N, K)
+    C = run_gemm(A, fa, sA, ma, B, fb, sB, mb, M, N, K, out=mxq.OUT_PRECISE)
+    Cref, Cabs = O.gemm(A, fa, sA, ma, B, fb, sB, mb, M, N, K)
+    check_gemm(C, Cref, Cabs, f"precise f{fa}{fb} m{ma}{mb}")
+
+
+def test_gemm_precise_wide_scales_nan_and_bf16_out():
+    """Scale bytes over 80..170 (dequantized operands from about 2^-63 to
+    2^59, sums up to about 2^110, inside fp32), a NaN code and a NaN scale,
+    fp32 and bf16 outputs."""
+    g = np.random.Generator(np.random.PCG64(1650))
+    M, N, K = 96, 160, 512
+    A, _ = rand_operand(g, 0, 1, M, K)
+    B, _ = rand_operand(g, 1, 1, N, K)
+    sA = g.integers(80, 171, size=(M, K // 32), dtype=np.uint8)
+    sB = g.integers(80, 171, size=(N, K // 32), dtype=np.uint8)
+    A[5, 17] = 0x7F
+    sB[9, 3] = 0xFF
+    C = run_gemm(A, 0, sA, 1, B, 1, sB, 1, M, N, K, out=mxq.OUT_PRECISE)
+    Cref, Cabs = O.gemm(A, 0, sA, 1, B, 1, sB, 1, M, N, K)
+    check_gemm(C, Cref, Cabs, "precise wide")
+    Cb = run_gemm(A, 0, sA, 1, B, 1, sB, 1, M, N, K, out=mxq.OUT_BF16 | mxq.OUT_PRECISE)
+    Cf = (Cb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ok = ~np.isnan(Cref)
+    assert np.array_equal(np.isnan(Cf), ~ok)
+    # bf16 keeps 8 significant bits: RNE moves a value by at most 2^-8 of itself
+    assert np.all(np.abs(Cf - Cref)[ok] <= (2.0 ** -8 * np.abs(Cref) + 2e-5 * Cabs)[ok])
+
+
+def test_gemm_precise_tiny_operands():
+    """Dequantized A operands between 2^-130 and 2^-118 (scale bytes 0..8,
+    byte 0 being 2^-127) against B near 2^123: every A value is a multiple of
+    2^-130, so its bf16 form is exact, subnormal or not, and so is the sum."""
+    g = np.random.Generator(np.random.PCG64(1660))
+    M, N, K = 64, 96, 256
+    A = g.integers(0x38, 0x40, size=(M, K), dtype=np.uint8)          # E4M3 values in [1, 2)
+    A[g.random((M, K)) < 0.5] |= 0x80
+    sA = g.integers(0, 9, size=(M, K // 32), dtype=np.uint8)
+    B = g.integers(0x38, 0x40, size=(N, K), dtype=np.uint8)
+    sB = g.integers(245, 252, size=(N, K // 32), dtype=np.uint8)
+    C = run_gemm(A, 0, sA, 1, B, 0, sB, 1, M, N, K, out=mxq.OUT_PRECISE)
+    Cref, Cabs = O.gemm(A, 0, sA, 1, B, 0, sB, 1, M, N, K)
+    check_gemm(C, Cref, Cabs, "precise tiny")
+
+
+def test_grouped_gemm_precise():
+    g = np.random.Generator(np.random.PCG64(1700))
+    G, N, K = 5, 192, 384
+    sizes = [40, 0, 131, 7, 64]
+    off = np.zeros(G + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    R = int(off[-1])
+    A, sA = rand_operand(g, 0, 2, R, K)
+    Bs = [rand_operand(g, 0, 1, N, K) for _ in range(G)]
+    B = np.stack([b for b, _ in Bs])
+    sB = np.stack([s for _, s in Bs])
+    C = torch.empty((R, N), dtype=torch.float32, device="cuda")
+    mxq.grouped_scaled_gemm(dev_u8(A), 0, dev_u8(sA), 2, dev_u8(B), 0, dev_u8(sB), 1,
+                            torch.from_numpy(off).cuda(), G, R, N, K, C, out=mxq.OUT_PRECISE)
+    m_idx = np.repeat(np.arange(R), N)
+    n_idx = np.tile(np.arange(N), R)
+    c, cabs = O.grouped_gemm_entries(A, 0, sA, 2, B, 0, sB, 1, off, N, K, m_idx, n_idx)
+    check_gemm(host(C), c.reshape(-1, N), cabs.reshape(-1, N), "grouped precise")
+
+
+@pytest.mark.parametrize("out", [0, 16])
+def test_gemm_blk128_last_row_in_partial_word(out):
+    """BLK128 A of 131 rows, K = 384: 393 scale bytes, so the last row's
+    bytes sit in a 4-byte word that the array only partly covers."""
+    g = np.random.Generator(np.random.PCG64(1750 + out))
+    M, N, K = 131, 64, 384
+    A, sA = rand_operand(g, 0, 2, M, K)
+    B, sB = rand_operand(g, 1, 1, N, K)
+    C = run_gemm(A, 0, sA, 2, B, 1, sB, 1, M, N, K, out=out)
+    Cref, Cabs = O.gemm(A, 0, sA, 2, B, 1, sB, 1, M, N, K)
+    hb = None if out else full_bound(A, 0, sA, 2, B, 1, sB, 1, M, N, K)
+    check_gemm(C, Cref, Cabs, f"blk128 partial word out={out}", hw_bound=hb)
 
 
 def test_gemm_deterministic():
