@@ -154,6 +154,37 @@ __device__ __forceinline__ uint32_t cast2_sat_f32(float y0, float y1) {
     return r;
 }
 
+// --- streaming memory access ----------------------------------------------------
+// The casts read every input once and write every output once.  They use
+// nontemporal loads and stores (the instructions' nt cache policy), which
+// keep these streams from displacing cached lines; on gfx950 a 2:1 stream
+// measured about 5.7 TB/s this way against about 3.3 TB/s with plain ones.
+typedef unsigned nt_v4u __attribute__((ext_vector_type(4)));
+typedef unsigned nt_v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+    const nt_v4u v = __builtin_nontemporal_load(reinterpret_cast<const nt_v4u*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_nt8(const void* p) {
+    const nt_v2u v = __builtin_nontemporal_load(reinterpret_cast<const nt_v2u*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld_nt4(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ void st_nt16(void* p, uint4 v) {
+    __builtin_nontemporal_store(nt_v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_v4u*>(p));
+}
+__device__ __forceinline__ void st_nt8(void* p, uint2 v) {
+    __builtin_nontemporal_store(nt_v2u{v.x, v.y}, reinterpret_cast<nt_v2u*>(p));
+}
+__device__ __forceinline__ void st_nt4(void* p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void st_nt1(void* p, uint8_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint8_t*>(p));
+}
+
 // --- reductions ----------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
