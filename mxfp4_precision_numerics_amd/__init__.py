@@ -8,6 +8,7 @@ HIP stream to the C entry point of the same name (``mxq_<name>``) and raises
 is not built, the first call raises.
 """
 import ctypes
+import dataclasses
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -135,3 +136,64 @@ def grouped_scaled_gemm(A, fa, sA, ma, B, fb, sB, mb, group_off, G, total_rows, 
     st = lib().mxq_grouped_scaled_gemm(_ptr(A), fa, _ptr(sA), ma, _ptr(B), fb, _ptr(sB), mb, _ptr(group_off), G,
                                        total_rows, N, K, _ptr(C), out, _stream(stream))
     _check("mxq_grouped_scaled_gemm", st)
+
+
+# --------------------------------------------------------------------------
+# Delayed-scaling recipe (argument marshalling around quantize_per_tensor)
+
+HYBRID = "HYBRID"  # E4M3 in the forward pass, E5M2 for gradients
+
+
+@dataclasses.dataclass(frozen=True)
+class DelayedScaling:
+    """The delayed-scaling recipe of the FP8 guide ("Transformer Engine: a
+    fundacao de software"): each step's scale comes from the largest amax of
+    the previous ``amax_history_len`` steps (``amax_compute_algo="max"``)
+    with margin 0; ``fmt`` HYBRID casts forward tensors to E4M3 and
+    gradients to E5M2.  The library computes scale = F_max / amax, so only
+    margin 0 and the "max" reduction are accepted."""
+    margin: int = 0
+    fmt: str = HYBRID
+    amax_history_len: int = 16
+    amax_compute_algo: str = "max"
+
+    def __post_init__(self):
+        if self.margin != 0:
+            raise ValueError("only margin 0 is supported")
+        if self.amax_compute_algo != "max":
+            raise ValueError("only amax_compute_algo='max' is supported")
+        if self.fmt not in (HYBRID, "E4M3", "E5M2"):
+            raise ValueError("fmt must be HYBRID, E4M3 or E5M2")
+        if not 1 <= self.amax_history_len <= 1024:
+            raise ValueError("amax_history_len must be in 1 .. 1024")
+
+    def format_for(self, backward=False):
+        """FP8 format of a forward tensor (backward=False) or a gradient."""
+        if self.fmt == HYBRID:
+            return E5M2 if backward else E4M3
+        return E4M3 if self.fmt == "E4M3" else E5M2
+
+
+class ScalingState:
+    """One tensor's delayed-scaling state on the GPU: the amax history
+    (float32 [amax_history_len], zeros at the start, so the first step uses
+    scale 1) and the last amax, scale and scale_inv (float32 [1] each).
+    quantize() casts with the scale from the history and then records this
+    step's amax in it, all inside mxq_quantize_per_tensor."""
+
+    def __init__(self, recipe, device="cuda"):
+        import torch
+        self.recipe = recipe
+        f32 = dict(dtype=torch.float32, device=device)
+        self.history = torch.zeros(recipe.amax_history_len, **f32)
+        self.amax = torch.zeros(1, **f32)
+        self.scale = torch.ones(1, **f32)
+        self.scale_inv = torch.ones(1, **f32)
+
+    def quantize(self, x, q_row=None, q_col=None, backward=False, stream=None):
+        """Cast ``x`` into the preallocated ``q_row`` / ``q_col``; returns
+        the FP8 format used."""
+        fmt = self.recipe.format_for(backward)
+        quantize_per_tensor(x, fmt, self.amax, self.scale, self.scale_inv, q_row, q_col,
+                            amax_history=self.history, stream=stream)
+        return fmt

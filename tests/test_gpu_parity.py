@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 import mxfp4_precision_numerics_amd as mxq
-from gpu_helpers import (check_gemm, dev_f32, dev_u8, empty_u8, gemm_scale_arg, gpu_quantize_mx,
+from gpu_helpers import (check_gemm, dev_bf16, dev_f32, dev_u8, empty_u8, gemm_scale_arg, gpu_quantize_mx,
                          gpu_quantize_per_tensor, host, mfma_bound, require_gpu, same_float)
 
 pytestmark = pytest.mark.gpu
@@ -35,6 +35,12 @@ def rand_bf16(g, shape, lo_exp=-140, hi_exp=130):
 
 
 # ------------------------------------------------------------------ per-tensor
+
+def synth_bf16(x):
+    """float32 values -> bf16 bit patterns (RNE)."""
+    u = np.asarray(x, np.float32).view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
 
 def compare_pt(got, exp, what):
     assert same_float(got["amax"], exp["amax"]), (what, got["amax"], exp["amax"])
@@ -112,6 +118,28 @@ def test_delayed_sequence_matches_oracle():
         exp = O.quantize_per_tensor(x, 1, history=ho, row=True, col=True)
         compare_pt(got, exp, f"step {t}")
         assert np.array_equal(hg, ho)
+
+
+def test_recipe_state_hybrid_forward_backward():
+    """ScalingState under the default DelayedScaling recipe: the forward
+    tensor is cast to E4M3 and the gradient to E5M2, each with its own
+    history, for 18 steps (beyond the history length), against the oracle."""
+    recipe = mxq.DelayedScaling()
+    fwd, bwd = mxq.ScalingState(recipe), mxq.ScalingState(recipe)
+    ho_f, ho_b = np.zeros(16, np.float32), np.zeros(16, np.float32)
+    for t in range(18):
+        g = np.random.Generator(np.random.PCG64([11, t]))
+        xf = synth_bf16(g.standard_normal((32, 128)).astype(np.float32) * (1 + t))
+        z = g.standard_normal((32, 128)).astype(np.float32)
+        xb = synth_bf16(np.exp2(3 * z - t % 5) * np.where(g.integers(0, 2, z.shape) == 0, 1, -1))
+        for state, x, ho, back in ((fwd, xf, ho_f, False), (bwd, xb, ho_b, True)):
+            q = empty_u8(32, 128)
+            fmt = state.quantize(dev_bf16(x), q_row=q, backward=back)
+            assert fmt == (mxq.E5M2 if back else mxq.E4M3)
+            exp = O.quantize_per_tensor(x, fmt, history=ho, row=True)
+            assert np.array_equal(host(q), exp["q_row"]), f"step {t} backward={back}"
+            assert host(state.scale_inv)[0] == exp["scale_inv"]
+            assert np.array_equal(host(state.history), ho)
 
 
 def test_per_tensor_strided_input():
