@@ -61,6 +61,8 @@ def lib():
         L.or_quantize_mx.argtypes = [_p, _i, _i64, _i64, _i64, _i, _p, _p, _p, _p]
         L.or_repack_fp4_to_fp8.restype = None
         L.or_repack_fp4_to_fp8.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p]
+        L.or_fp4_row_to_fp8_col.restype = None
+        L.or_fp4_row_to_fp8_col.argtypes = [_p, _p, _i64, _i64, _p, _p]
         L.or_dequant.restype = ctypes.c_double
         L.or_dequant.argtypes = [_p, _i, _p, _i, _i64, _i64, _i64]
         L.or_gemm_entries.restype = None
@@ -197,6 +199,20 @@ def repack_fp4_to_fp8(q4, s4, idx=None, rows=None):
     q8 = np.empty((rows, cols), np.uint8)
     s8 = np.empty((rows, cols // 128), np.uint8)
     lib().or_repack_fp4_to_fp8(_ptr(q4), _ptr(s4), _ptr(idx), src_rows, rows, cols, _ptr(q8), _ptr(s8))
+    return q8, s8
+
+
+# --- O7b -------------------------------------------------------------------
+
+def fp4_row_to_fp8_col(q4, s4):
+    """MXFP4 rows [rows, cols] -> MX E4M3 columns: (q8 [cols, rows], s8 [cols, rows/32])."""
+    q4 = np.ascontiguousarray(q4, dtype=np.uint8)
+    s4 = np.ascontiguousarray(s4, dtype=np.uint8)
+    rows, cols = q4.shape[0], q4.shape[1] * 2
+    assert rows % 32 == 0 and cols % 32 == 0 and s4.shape == (rows, cols // 32)
+    q8 = np.empty((cols, rows), np.uint8)
+    s8 = np.empty((cols, rows // 32), np.uint8)
+    lib().or_fp4_row_to_fp8_col(_ptr(q4), _ptr(s4), rows, cols, _ptr(q8), _ptr(s8))
     return q8, s8
 
 

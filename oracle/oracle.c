@@ -511,6 +511,41 @@ void or_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const int32_t* i
 }
 
 /* ------------------------------------------------------------------------ */
+/* O7b. FP4 row -> FP8 col: dequantize, transpose, requantize.              */
+/* [MoE FP4], "Metodologia", "Kernels CUDA Otimizados": besides the row-    */
+/* layout conversion, one kernel fuses the FP4 dequantization, the matrix   */
+/* transpose and the FP8 requantization, so that activations cached in      */
+/* MXFP4 (row blocks along the hidden dimension) feed the weight-gradient   */
+/* GEMM, whose contraction runs over the tokens.                             */
+/* Readings: the dequantization is exact (E2M1 value times 2^(s-127), a     */
+/* double); the requantization is MX block-32 E4M3 along the new rows (the  */
+/* old columns, 32 tokens per block) by quantize_block32's rule; a source   */
+/* block with scale byte 0xFF dequantizes to NaN, so every output block it  */
+/* reaches is a NaN block.  In: q4 [rows, cols/2], s4 [rows, cols/32].      */
+/* Out: q8 [cols, rows], s8 [cols, rows/32]; rows % 32 == 0, cols % 32 == 0. */
+/* ------------------------------------------------------------------------ */
+void or_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, int64_t cols, uint8_t* q8,
+                           uint8_t* s8)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; ++c) {
+        double v[32];
+        unsigned codes[32];
+        for (int64_t b = 0; b < rows / 32; ++b) {
+            for (int i = 0; i < 32; ++i) {
+                int64_t r = b * 32 + i;
+                uint8_t byte = q4[r * (cols / 2) + c / 2];
+                unsigned code = (c & 1) ? (byte >> 4) : (byte & 0xFu);
+                v[i] = or_value(OR_E2M1, code) * or_e8m0_value(s4[r * (cols / 32) + c / 32]);
+            }
+            s8[c * (rows / 32) + b] = (uint8_t)quantize_block32(OR_E4M3, v, codes);
+            for (int i = 0; i < 32; ++i)
+                q8[c * rows + b * 32 + i] = (uint8_t)codes[i];
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* O8. Dequantization of one operand element.                               */
 /* Element k of row i of an operand stored [rows, K] (E2M1: [rows, K/2]),    */
 /* with its scale: per-tensor (a float scale_inv), or one E8M0 byte per 32   */

@@ -190,3 +190,74 @@ def test_repack_matches_mx_quantize_of_dequant(O):
     exact_rows = np.all(gap <= 8, axis=1)
     assert exact_rows.any()
     assert np.array_equal(d8[exact_rows], d4[exact_rows])
+
+
+# --- O7b: FP4 row -> FP8 col --------------------------------------------------
+
+# E2M1 from its definition (sign bit 3; exponent bits 2..1, bias 1; one
+# mantissa bit; exponent field 0 is subnormal 0.5 * m)
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _fp4_col_reference(q4, s4):
+    """Exact dequant in float64, transpose, MX E4M3 along the new rows:
+    e = floor(log2 amax) - 8 clamped to [-127, 127]; codes = RNE of the
+    saturated v / 2^e by torch's float8_e4m3fn cast."""
+    rows, half = q4.shape
+    cols = 2 * half
+    nib = np.empty((rows, cols), np.uint8)
+    nib[:, 0::2], nib[:, 1::2] = q4 & 0xF, q4 >> 4
+    mag = _E2M1[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+    sc = np.exp2(s4.astype(np.float64) - 127.0)
+    sc[s4 == 0xFF] = np.nan
+    v = (mag * np.repeat(sc, 32, axis=1)).T.reshape(cols, rows // 32, 32)   # [cols, blocks, 32]
+    amax = np.nanmax(np.abs(v), axis=2)
+    bad = np.isnan(v).any(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(amax)) - 8
+    e = np.where(amax == 0, -127, np.clip(e, -127, 127))
+    y = np.clip(v / np.exp2(e)[..., None], -448.0, 448.0)
+    codes = _tq(np.nan_to_num(y), torch.float8_e4m3fn).reshape(cols, rows // 32, 32)
+    codes[bad] = 0x7F
+    sbyte = np.where(bad, 0xFF, e + 127).astype(np.uint8)
+    return codes.reshape(cols, rows), sbyte
+
+
+def test_fp4_col_matches_independent_reference(O):
+    g = np.random.Generator(np.random.PCG64(27))
+    for lo, hi in ((120, 135), (0, 255), (200, 255)):
+        q4 = g.integers(0, 256, size=(96, 48), dtype=np.uint8)
+        s4 = g.integers(lo, hi, size=(96, 3), dtype=np.uint8)
+        q8, s8 = O.fp4_row_to_fp8_col(q4, s4)
+        rq, rs = _fp4_col_reference(q4, s4)
+        assert np.array_equal(s8, rs), (lo, hi)
+        assert np.array_equal(q8, rq), (lo, hi)
+
+
+def test_fp4_col_specials(O):
+    q4 = np.zeros((64, 16), np.uint8)
+    s4 = np.full((64, 1), 127, np.uint8)
+    q4[3, 0] = 0x98            # row 3: column 0 = -0 (code 8), column 1 = -0.5 (code 9)
+    s4[40, 0] = 0xFF           # row 40: a NaN source block covering every column
+    q8, s8 = O.fp4_row_to_fp8_col(q4, s4)
+    # column 0, rows 0..31: only zeros -> byte 0 (e = -127); -0 keeps its sign
+    assert s8[0, 0] == 0 and q8[0, 3] == 0x80 and np.count_nonzero(q8[0, :32]) == 1
+    # column 1, rows 0..31: amax 0.5 -> e = floor(log2 0.5) - 8 = -9; -0.5 / 2^-9 = -256 = E4M3 0xF8
+    assert s8[1, 0] == 127 - 9 and q8[1, 3] == 0xF8
+    # rows 32..63 of every column hold row 40's NaN: NaN blocks
+    assert np.all(s8[:, 1] == 0xFF) and np.all(q8[:, 32:] == 0x7F)
+    # the remaining columns of rows 0..31 are all zero
+    assert np.all(s8[2:, 0] == 0) and np.all(q8[2:, :32] == 0)
+
+
+def test_fp4_col_lossless_when_block_scales_agree(O):
+    """When the 32 source rows of an output block share one scale byte, the
+    requantized values equal the source values exactly (E2M1 values are E4M3
+    values shifted by a power of two)."""
+    g = np.random.Generator(np.random.PCG64(28))
+    q4 = g.integers(0, 256, size=(64, 32), dtype=np.uint8)
+    s4 = np.repeat(g.integers(1, 250, size=(2, 2), dtype=np.uint8), 32, axis=0)
+    q8, s8 = O.fp4_row_to_fp8_col(q4, s4)
+    d4 = O.dequant_matrix(q4, O.E2M1, s4, O.SCALE_BLK32, 64, 64)
+    d8 = O.dequant_matrix(q8, O.E4M3, s8, O.SCALE_BLK32, 64, 64)
+    assert np.array_equal(d8.T, d4) and np.array_equal(np.signbit(d8.T), np.signbit(d4))
