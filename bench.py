@@ -251,7 +251,11 @@ def measure_rows(torch, mxq, synth, dev, reps):
     idx_d = torch.from_numpy(idx).to(dev)
     ms = timed(lambda: mxq.repack_fp4_to_fp8(q4, s4, q8, s8, gather_idx=idx_d))
     rows[f"a5 FP4->FP8 repack with gather, R={R} rows x 7168"] = bw(R * (3584 + 224 + 4 + 7168 + 56), ms)
-    del x
+    q8c, s8c = torch.empty((7168, 8192), **u8), torch.empty((7168, 256), **u8)
+    ms = timed(lambda: mxq.fp4_row_to_fp8_col(q4, s4, q8c, s8c))
+    rows["f1 FP4 row -> FP8 col (dequant, transpose, MX E4M3), X 8192x7168"] = bw(
+        x.numel() * (0.5 + 1 / 32 + 1 + 1 / 32), ms)
+    del x, q8c, s8c
     qw = torch.empty((32, 4096, 7168), **u8)
     sw4 = torch.empty((32, 4096, 224), **u8)
     for e in range(32):

@@ -155,6 +155,28 @@ int mxq_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const int32_t* g
                           int64_t rows, int64_t cols, uint8_t* q8, uint8_t* s8, void* stream);
 
 /*
+ * mxq_fp4_row_to_fp8_col - MXFP4 rows -> transposed MX E4M3 (block 32 along
+ * the new rows), fused: exact dequantization, transpose, requantization.
+ *
+ * Defines: [MoE FP4], "Metodologia", "Kernels CUDA Otimizados" (besides the
+ * row-layout conversion, a kernel fuses FP4 dequantization, the matrix
+ * transpose and FP8 requantization, so that MXFP4-cached activations feed
+ * the weight-gradient GEMM, which contracts over the tokens).
+ *  q4, s4  source MXFP4 codes [rows, cols/2] (element 2j in the low nibble)
+ *          and E8M0 scales [rows, cols/32]; 0xFF (NaN) makes every output
+ *          block that holds one of its elements a NaN block.
+ *  q8, s8  outputs: E4M3 codes [cols, rows] and E8M0 [cols, rows/32].
+ * Each output block of 32 source rows: e = floor(log2 amax) - 8 clamped to
+ * [-127, 127] over the exact values v = E2M1(code) * 2^(s-127) (all zero:
+ * e = -127); codes = saturating RNE E4M3 of v / 2^e; a NaN block gets byte
+ * 0xFF and codes 0x7F.
+ * Rules: rows % 32 == 0, cols % 32 == 0; q4 and q8 16-byte aligned.  The
+ * call writes every byte of q8 and s8 and reads nothing else.
+ */
+int mxq_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, int64_t cols, uint8_t* q8,
+                           uint8_t* s8, void* stream);
+
+/*
  * mxq_scaled_gemm - C = dequant(A) . dequant(B)^T with fp32 accumulation on
  * gfx950's block-scaled MFMA.
  *

@@ -48,6 +48,8 @@ def lib():
         L.mxq_quantize_mx.argtypes = [p, i, i64, i64, i64, i, p, p, p, p, p]
         L.mxq_repack_fp4_to_fp8.restype = i
         L.mxq_repack_fp4_to_fp8.argtypes = [p, p, p, i64, i64, i64, p, p, p]
+        L.mxq_fp4_row_to_fp8_col.restype = i
+        L.mxq_fp4_row_to_fp8_col.argtypes = [p, p, i64, i64, p, p, p]
         L.mxq_scaled_gemm.restype = i
         L.mxq_scaled_gemm.argtypes = [p, i, p, i, p, i, p, i, i64, i64, i64, p, i, i64, p]
         L.mxq_grouped_scaled_gemm.restype = i
@@ -120,6 +122,14 @@ def repack_fp4_to_fp8(q4, s4, q8, s8, gather_idx=None, stream=None):
     st = lib().mxq_repack_fp4_to_fp8(_ptr(q4), _ptr(s4), _ptr(gather_idx), src_rows, rows, cols, _ptr(q8),
                                      _ptr(s8), _stream(stream))
     _check("mxq_repack_fp4_to_fp8", st)
+
+
+def fp4_row_to_fp8_col(q4, s4, q8, s8, stream=None):
+    """MXFP4 rows [rows, cols] -> MX E4M3 columns q8 [cols, rows], s8
+    [cols, rows/32] (mxq_fp4_row_to_fp8_col)."""
+    rows, cols = q4.shape[0], q4.shape[1] * 2
+    st = lib().mxq_fp4_row_to_fp8_col(_ptr(q4), _ptr(s4), rows, cols, _ptr(q8), _ptr(s8), _stream(stream))
+    _check("mxq_fp4_row_to_fp8_col", st)
 
 
 def scaled_gemm(A, fa, sA, ma, B, fb, sB, mb, M, N, K, C, out=OUT_F32, ldc=None, stream=None):

@@ -15,6 +15,8 @@ hipError_t launch_quantize_mx(const void* x, int src, int64_t rows, int64_t cols
 
 hipError_t launch_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const int32_t* idx, int64_t src_rows,
                                     int64_t rows, int64_t cols, uint8_t* q8, uint8_t* s8, hipStream_t st);
+hipError_t launch_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, int64_t cols, uint8_t* q8,
+                                     uint8_t* s8, hipStream_t st);
 
 // Dense (group_off == nullptr) or grouped scaled GEMM.
 struct GemmArgs {

@@ -98,6 +98,17 @@ int mxq_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const int32_t* g
                                                     as_stream(stream)));
 }
 
+int mxq_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, int64_t cols, uint8_t* q8,
+                           uint8_t* s8, void* stream) {
+    if (rows < 0 || cols < 0) return MXQ_ERR_SHAPE;
+    if (!q4 || !s4 || !q8 || !s8) return MXQ_ERR_NULL;
+    if (rows % 32 != 0 || cols % 32 != 0) return MXQ_ERR_SHAPE;
+    if ((rows + 127) / 128 > MAX_GRID_Y) return MXQ_ERR_SHAPE;
+    if (!aligned16(q4) || !aligned16(q8)) return MXQ_ERR_ALIGN;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    return hip_status(mxq::launch_fp4_row_to_fp8_col(q4, s4, rows, cols, q8, s8, as_stream(stream)));
+}
+
 // The GEMM kernel addresses each operand (per group) and its scale array
 // with 32-bit byte offsets.
 static bool below_4gib(int64_t rows, int64_t K, int fmt, int mode) {

@@ -104,4 +104,132 @@ hipError_t launch_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// FP4 row -> FP8 col.  MoE FP4 page, "Metodologia", "Kernels CUDA
+// Otimizados": one kernel dequantizes cached MXFP4 activations, transposes
+// them and requantizes them to FP8, so that the weight-gradient GEMM (which
+// contracts over the tokens) reads FP8 blocks along the tokens.  Reading:
+// exact dequantization, then MX block-32 E4M3 along the new rows.
+//
+// A block of 256 threads owns a tile of 128 source rows x 256 source columns.
+//  Row phase: wave w, step it reads source row 16*it + 4*w + l/16, 16 lanes
+//  per row, 16 codes (8 bytes) per lane: whole 128-byte lines.  Codes go to
+//  LDS as they are (4 bits each); the row's 8 scale bytes too.
+//  Column phase (twice, for columns 0..127 and 128..255 of the tile): lane l
+//  of wave w takes source rows 8*(l/4) .. +7 and columns 8*(4w + l%4) .. +7,
+//  i.e. 8 output rows of 8 tokens; the 16 lanes of a column cover its 128
+//  tokens and write a whole line.  An output block (32 tokens) spans the 4
+//  lanes that differ in lane bits 2-3.
+// Each element is m * 2^(s-127) with m an E2M1 value; its exponent is that of
+// m plus s - 127, so the block exponent is an integer max and every element
+// divided by the block scale is m * 2^(s-127-e), exact in binary32 where it
+// can reach E4M3's range, then saturated at 448 and rounded to nearest even.
+// LDS rows hold 32 dwords of codes; dword index bits 2-4 are XOR-ed with the
+// row's bits 3-5, which halves the column reads' bank conflicts to 2-way.
+// ---------------------------------------------------------------------------
+constexpr int FC_ROWS = 128, FC_COLS = 256;
+
+__device__ __forceinline__ int fc_swz(int r, int dw) { return dw ^ (((r >> 3) & 7) << 2); }
+
+__global__ void __launch_bounds__(256) k_fp4_row_to_fp8_col(const uint8_t* __restrict__ q4,
+                                                            const uint8_t* __restrict__ s4, int64_t rows,
+                                                            int64_t cols, uint8_t* __restrict__ q8,
+                                                            uint8_t* __restrict__ s8) {
+    __shared__ __attribute__((aligned(16))) uint32_t codes[FC_ROWS * 32];
+    __shared__ uint8_t scales[FC_ROWS * 8];
+    const int64_t tr = (int64_t)blockIdx.y * FC_ROWS, tc = (int64_t)blockIdx.x * FC_COLS;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int ch = lane & 15;
+    {
+        uint2 c[8];
+        uint8_t sb[8];
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int r = 16 * it + 4 * w + (lane >> 4);
+            const bool rok = tr + r < rows;
+            c[it] = make_uint2(0u, 0u);
+            sb[it] = 0;
+            if (rok && tc + 16 * ch < cols) c[it] = ld_nt8(q4 + (tr + r) * (cols / 2) + tc / 2 + 8 * ch);
+            if (rok && ch < 8 && tc + 32 * ch < cols) sb[it] = s4[(tr + r) * (cols / 32) + tc / 32 + ch];
+        }
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int r = 16 * it + 4 * w + (lane >> 4);
+            *reinterpret_cast<uint2*>(&codes[r * 32 + fc_swz(r, 2 * ch)]) = c[it];
+            if (ch < 8) scales[r * 8 + ch] = sb[it];
+        }
+    }
+    __syncthreads();
+    const int g = lane >> 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int cg = 16 * h + 4 * w + (lane & 3);  // 8-column group of the tile, 0..31
+        uint32_t d[8];
+        int sc[8];
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * g + i;
+            d[i] = codes[r * 32 + fc_swz(r, cg)];
+            sc[i] = scales[r * 8 + (cg >> 2)];
+            bad |= sc[i] == 0xFF;
+        }
+        bad = quad4_max_u32(bad ? 1u : 0u) != 0u;  // the block's 32 tokens
+        // block exponent per column: max over non-zero elements of
+        // ex(m) + s - 127, kept as E + 512 (0: no non-zero element)
+        uint32_t emax[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int k = (d[i] >> (4 * j)) & 7;
+                const int ex = k == 1 ? -1 : (k >> 1) - 1;
+                const uint32_t E = k == 0 ? 0u : (uint32_t)(ex + sc[i] - 127 + 512);
+                m = m > E ? m : E;
+            }
+            emax[j] = quad4_max_u32(m);
+        }
+        const int64_t c0 = tc + 8 * cg;
+        const bool live = tr + 8 * g < rows && c0 < cols;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int e = emax[j] == 0 ? -127 : (int)emax[j] - 512 - 8;  // E4M3: emax 8
+            e = e < -127 ? -127 : (e > 127 ? 127 : e);
+            float y[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t n = (d[i] >> (4 * j)) & 0xF;
+                const uint32_t k = n & 7;
+                // |m| as binary32: 0, 0.5, then (1 + (k&1)/2) * 2^((k>>1)-1)
+                const uint32_t mb = k == 0 ? 0u : (k == 1 ? 0x3F000000u : ((((k >> 1) + 126u) << 23) | ((k & 1u) << 22)));
+                // a non-zero element has dsh <= 9; a zero one (in an all-zero
+                // block, e = -127) can reach 254: clamp into exp2i's range.
+                // Below 2^-127 every value rounds to 0 in E4M3.
+                int dsh = sc[i] - 127 - e;
+                dsh = dsh < -127 ? -127 : (dsh > 127 ? 127 : dsh);
+                float v = as_float(mb) * exp2i(dsh);
+                v = v < 448.0f ? v : 448.0f;    // saturate
+                y[i] = (n & 8) ? -v : v;
+            }
+            uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
+            uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+            hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
+            if (bad) { lo = 0x7F7F7F7Fu; hi = 0x7F7F7F7Fu; }
+            if (live) {
+                st_nt8(q8 + (c0 + j) * rows + tr + 8 * g, make_uint2(lo, hi));
+                if ((g & 3) == 0) s8[(c0 + j) * (rows / 32) + (tr + 8 * g) / 32] = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
+            }
+        }
+    }
+}
+
+hipError_t launch_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, int64_t cols, uint8_t* q8,
+                                     uint8_t* s8, hipStream_t st) {
+    const dim3 grid((unsigned)((cols + FC_COLS - 1) / FC_COLS), (unsigned)((rows + FC_ROWS - 1) / FC_ROWS));
+    hipLaunchKernelGGL(k_fp4_row_to_fp8_col, grid, dim3(256), 0, st, q4, s4, rows, cols, q8, s8);
+    return hipGetLastError();
+}
+
 }  // namespace mxq

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 7
+    assert len(names) == 8
     for n in names:
         assert hasattr(L, n), n
 
@@ -93,6 +93,18 @@ def test_repack_validation(L):
     assert f(None, P, None, 4, 4, 128, P, P, None) == ENULL
     assert f(P, P, P + 2, 4, 4, 128, P, P, None) == EALIGN
     assert f(P, P, P, 4, 0, 128, P, P, None) == OK
+
+
+def test_fp4_col_validation(L):
+    f = L.mxq_fp4_row_to_fp8_col
+    assert f(P, P, 48, 64, P, P, None) == ESHAPE        # rows % 32
+    assert f(P, P, 64, 48, P, P, None) == ESHAPE        # cols % 32
+    assert f(P, P, -32, 64, P, P, None) == ESHAPE
+    assert f(None, P, 64, 64, P, P, None) == ENULL
+    assert f(P, P, 64, 64, P, None, None) == ENULL
+    assert f(P + 8, P, 64, 64, P, P, None) == EALIGN
+    assert f(P, P, 64, 64, P + 8, P, None) == EALIGN
+    assert f(P, P, 0, 64, P, P, None) == OK
 
 
 def test_gemm_validation(L):

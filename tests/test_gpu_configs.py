@@ -159,6 +159,13 @@ def test_workload4_mxfp4_repack_grouped():
     oq4, os4, _, _ = O.quantize_mx(x, 2)
     assert np.array_equal(host(q4), oq4) and np.array_equal(host(s4), os4)
     log("workload 4: MXFP4 codes bit-exact")
+    # the backward-side twin: cached MXFP4 activations -> FP8 along the tokens
+    q8c, s8c = empty_u8(7168, 8192), empty_u8(7168, 256)
+    mxq.fp4_row_to_fp8_col(q4, s4, q8c, s8c)
+    oq8c, os8c = O.fp4_row_to_fp8_col(oq4, os4)
+    assert np.array_equal(host(q8c), oq8c) and np.array_equal(host(s8c), os8c)
+    del q8c, s8c, oq8c, os8c
+    log("workload 4: FP4 row -> FP8 col bit-exact")
     q8 = empty_u8(R, 7168)
     s8 = empty_u8(R, 56)
     mxq.repack_fp4_to_fp8(q4, s4, q8, s8, gather_idx=torch.from_numpy(idx).cuda())

@@ -289,6 +289,61 @@ def test_repack_random_with_gather(gather):
     assert np.array_equal(host(q8g), q8o)
 
 
+# ------------------------------------------------------- FP4 row -> FP8 col
+
+def gpu_fp4_col(q4, s4):
+    rows, cols = q4.shape[0], q4.shape[1] * 2
+    q8, s8 = empty_u8(cols, rows), empty_u8(cols, rows // 32)
+    mxq.fp4_row_to_fp8_col(dev_u8(q4), dev_u8(s4), q8, s8)
+    return host(q8), host(s8)
+
+
+@pytest.mark.parametrize("shape", [(128, 256), (96, 288), (224, 544), (32, 32), (256, 1024)])
+@pytest.mark.parametrize("srange", [(120, 136), (0, 255), (230, 255)])
+def test_fp4_col_random(shape, srange):
+    """Random codes and scale bytes (every code; scale spreads within a
+    block of up to 255 binades), ragged tiles both ways: bit-exact."""
+    rows, cols = shape
+    g = np.random.Generator(np.random.PCG64([17, rows, cols, srange[0]]))
+    q4 = g.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    s4 = g.integers(srange[0], srange[1], size=(rows, cols // 32), dtype=np.uint8)
+    q8, s8 = gpu_fp4_col(q4, s4)
+    oq, os_ = O.fp4_row_to_fp8_col(q4, s4)
+    assert np.array_equal(s8, os_)
+    assert np.array_equal(q8, oq)
+
+
+def test_fp4_col_specials():
+    g = np.random.Generator(np.random.PCG64(18))
+    rows, cols = 160, 320
+    q4 = g.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    s4 = g.integers(110, 140, size=(rows, cols // 32), dtype=np.uint8)
+    s4[37, 4] = 0xFF               # NaN source block
+    q4[64:96, :] = 0               # an all-zero band of tokens
+    q4[100, 10] = 0x88             # two negative zeros
+    s4[130:160, 2] = 0             # the smallest scale, 2^-127
+    s4[128:130, 2] = 254           # next to the largest
+    q4[0:32, 40:48] = 0            # zeros in rows with the largest scales
+    s4[0:32, 5] = 254
+    q8, s8 = gpu_fp4_col(q4, s4)
+    oq, os_ = O.fp4_row_to_fp8_col(q4, s4)
+    assert np.array_equal(s8, os_) and np.array_equal(q8, oq)
+    assert np.all(s8[128:160, 1] == 0xFF)
+
+
+def test_fp4_col_of_gpu_mx_quantize():
+    """BF16 activations -> MXFP4 rows (GPU) -> FP8 columns (GPU) against the
+    oracle's own chain."""
+    g = np.random.Generator(np.random.PCG64(19))
+    x = synth_bf16(g.standard_normal((512, 1024)).astype(np.float32) * np.exp2(g.integers(-4, 5, (1, 1024))))
+    q4, s4, _, _ = gpu_quantize_mx(x, mxq.E2M1)
+    oq4, os4, _, _ = O.quantize_mx(x, O.E2M1)
+    assert np.array_equal(q4, oq4) and np.array_equal(s4, os4)
+    q8, s8 = gpu_fp4_col(q4, s4)
+    oq, os_ = O.fp4_row_to_fp8_col(oq4, os4)
+    assert np.array_equal(s8, os_) and np.array_equal(q8, oq)
+
+
 # ------------------------------------------------------------------ GEMM
 
 def rand_operand(g, fmt, mode, rows, K, nan_codes=False):
