@@ -122,8 +122,9 @@ hipError_t launch_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const 
 //  lanes that differ in lane bits 2-3.
 // Each element is m * 2^(s-127) with m an E2M1 value; its exponent is that of
 // m plus s - 127, so the block exponent is an integer max and every element
-// divided by the block scale is m * 2^(s-127-e), exact in binary32 where it
-// can reach E4M3's range, then saturated at 448 and rounded to nearest even.
+// divided by the block scale is m * 2^(s-127-e), formed with ldexp (exact
+// where it can reach E4M3's range), saturated at 448 and rounded to nearest
+// even by the converter.
 // LDS rows hold 32 dwords of codes; dword index bits 2-4 are XOR-ed with the
 // row's bits 3-5, which halves the column reads' bank conflicts to 2-way.
 // ---------------------------------------------------------------------------
@@ -161,7 +162,7 @@ __global__ void __launch_bounds__(256) k_fp4_row_to_fp8_col(const uint8_t* __res
     }
     __syncthreads();
     const int g = lane >> 2;
-#pragma unroll
+#pragma unroll 1
     for (int h = 0; h < 2; ++h) {
         const int cg = 16 * h + 4 * w + (lane & 3);  // 8-column group of the tile, 0..31
         uint32_t d[8];
@@ -175,17 +176,18 @@ __global__ void __launch_bounds__(256) k_fp4_row_to_fp8_col(const uint8_t* __res
             bad |= sc[i] == 0xFF;
         }
         bad = quad4_max_u32(bad ? 1u : 0u) != 0u;  // the block's 32 tokens
-        // block exponent per column: max over non-zero elements of
-        // ex(m) + s - 127, kept as E + 512 (0: no non-zero element)
+        // Block exponent per column.  For a non-zero E2M1 magnitude code k
+        // (1..7: 0.5, 1, 1.5, 2, 3, 4, 6) floor(log2 |m|) + 1 = k >> 1, so an
+        // element's floor(log2 |v|) is (k >> 1) + s - 128; the max over the
+        // block is kept as (k >> 1) + s + 1 (0: no non-zero element).
         uint32_t emax[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             uint32_t m = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int k = (d[i] >> (4 * j)) & 7;
-                const int ex = k == 1 ? -1 : (k >> 1) - 1;
-                const uint32_t E = k == 0 ? 0u : (uint32_t)(ex + sc[i] - 127 + 512);
+                const uint32_t k = (d[i] >> (4 * j)) & 7u;
+                const uint32_t E = k != 0u ? (k >> 1) + (uint32_t)sc[i] + 1u : 0u;
                 m = m > E ? m : E;
             }
             emax[j] = quad4_max_u32(m);
@@ -194,23 +196,21 @@ __global__ void __launch_bounds__(256) k_fp4_row_to_fp8_col(const uint8_t* __res
         const bool live = tr + 8 * g < rows && c0 < cols;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            int e = emax[j] == 0 ? -127 : (int)emax[j] - 512 - 8;  // E4M3: emax 8
+            int e = emax[j] == 0u ? -127 : (int)emax[j] - 137;  // floor(log2 amax) - 8 (E4M3 emax)
             e = e < -127 ? -127 : (e > 127 ? 127 : e);
             float y[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t n = (d[i] >> (4 * j)) & 0xF;
-                const uint32_t k = n & 7;
-                // |m| as binary32: 0, 0.5, then (1 + (k&1)/2) * 2^((k>>1)-1)
-                const uint32_t mb = k == 0 ? 0u : (k == 1 ? 0x3F000000u : ((((k >> 1) + 126u) << 23) | ((k & 1u) << 22)));
-                // a non-zero element has dsh <= 9; a zero one (in an all-zero
-                // block, e = -127) can reach 254: clamp into exp2i's range.
-                // Below 2^-127 every value rounds to 0 in E4M3.
-                int dsh = sc[i] - 127 - e;
-                dsh = dsh < -127 ? -127 : (dsh > 127 ? 127 : dsh);
-                float v = as_float(mb) * exp2i(dsh);
-                v = v < 448.0f ? v : 448.0f;    // saturate
-                y[i] = (n & 8) ? -v : v;
+                const uint32_t n = (d[i] >> (4 * j)) & 0xFu;
+                const uint32_t k = n & 7u;
+                // 2|m| = 0, 1, 2, 3 for k < 4, else (2 + (k & 1)) << ((k >> 1) - 1)
+                const uint32_t hiv = ((2u + (k & 1u)) << ((k >> 1) & 3u)) >> 1;
+                const uint32_t two_m = k < 4u ? k : hiv;
+                // |v| / 2^e = 2|m| * 2^(s - 128 - e): exact where it can reach
+                // E4M3's range (ldexp of a 2-bit integer), zero stays zero
+                float v = __builtin_amdgcn_ldexpf((float)two_m, sc[i] - 128 - e);
+                v = v < 448.0f ? v : 448.0f;  // saturate
+                y[i] = as_float(as_uint(v) | ((n & 8u) << 28));
             }
             uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
             lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
