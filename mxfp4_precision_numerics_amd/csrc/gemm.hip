@@ -19,19 +19,23 @@
 // r % 4, column l % 32.  The instruction's op_sel picks which byte of the
 // 32-bit scale operand is used.
 //
-// Pipeline.  K runs in halves of 64 elements (one MFMA deep).  A block
-// (4 waves, 2 x 2 over the tile) keeps a ring of four LDS slots, one K half
-// of the A and B tiles each, and two slots of scale dwords (one per K step of
-// 128).  In half j every wave, after one barrier:
+// Pipeline.  K runs in halves of 64 elements (one MFMA deep), staged in
+// ring units of one K step (two halves) for operands of one kind (FP8 x FP8:
+// whole 128-byte lines per row; FP4 x FP4: 64 bytes) or of one half for
+// mixed FP4 x FP8.  A block (4 waves, 2 x 2 over the tile) keeps a ring of
+// NSL LDS slots of one unit of the A and B tiles each (two for the 256 x 256
+// FP8 tile, four or eight where they fit), and two slots of scale dwords (a
+// group of four K steps each).  In half j every wave:
 //   * runs the half's MFMAs from fragments already in registers,
-//   * reads the next half's fragments (slot j+1, landed) into the other
-//     register set, interleaved with the MFMAs,
-//   * starts the global->LDS copy of half j+3 into the slot read in half j-2.
-// So copies get two halves to land and LDS reads one half, both hidden
-// behind MFMAs.  The copies are buffer_load ... lds instructions issued from
-// inline assembly: the compiler's wait insertion cannot see them and so
-// adds no conservative waits; the kernel waits for them explicitly (vmcnt)
-// before the barrier that publishes a slot.
+//   * reads the next half's fragments (landed) into the other register set,
+//     interleaved with the MFMAs,
+//   * in the last half of unit u, after a barrier, starts the global->LDS
+//     copies of unit u + NSL into the slot unit u leaves.
+// So copies get NSL - 1 units minus one half to land and LDS reads one
+// half, both hidden behind MFMAs.  The copies are buffer_load ... lds
+// instructions issued from inline assembly: the compiler's wait insertion
+// cannot see them and so adds no conservative waits; the kernel waits for
+// them explicitly (vmcnt) before the barrier that publishes a slot.
 #include <utility>
 
 #include "common.h"
@@ -48,15 +52,15 @@ template <int F> struct OpInfo {
 };
 
 // LDS byte offset of 16-byte chunk `c` of row `r` in a slot whose rows hold
-// RB bytes (64: four chunks, 32: two).  gfx950's LDS serves a ds_read_b128
+// RB bytes (128: eight chunks, 64: four, 32: two).  gfx950's LDS serves a ds_read_b128
 // 16 lanes per clock from 64 four-byte banks (256 bytes), so 16 consecutive
 // lanes (16 consecutive rows of a fragment) must land on 16 distinct 16-byte
 // bank quads; the XOR swizzle on the row bits above those that already
 // spread it gives each of the 16 rows its own quad (measured: 4 clocks per
 // wave-wide read, against 8 without it).
 template <int RB> __device__ __forceinline__ int swz(int r) {
-    static_assert(RB == 64 || RB == 32, "LDS row bytes");
-    return (RB == 64) ? ((r >> 2) & 3) : ((r >> 3) & 1);
+    static_assert(RB == 128 || RB == 64 || RB == 32, "LDS row bytes");
+    return (RB == 128) ? ((r >> 1) & 7) : (RB == 64) ? ((r >> 2) & 3) : ((r >> 3) & 1);
 }
 template <int RB> __device__ __forceinline__ int lds_off(int r, int c) {
     return r * RB + ((c ^ swz<RB>(r)) << 4);
@@ -277,11 +281,13 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     static_assert(!PRECISE || (FA != E2M1 && FB != E2M1), "precise mode takes FP8 operands");
     using IA = OpInfo<FA>;
     using IB = OpInfo<FB>;
-    // Ring unit: SU K halves.  Copies fetch RB contiguous bytes per row; FP4
-    // rows would be only 32 bytes per half, and partial-line copies cost the
-    // CU's address unit about as much as full ones, so FP4 x FP4 stages a
-    // whole K step (64 bytes per row) per unit.
-    constexpr int SU = (FA == E2M1 && FB == E2M1) ? 2 : 1;
+    // Ring unit: SU K halves.  Copies fetch RB contiguous bytes per row, and
+    // partial-line copies cost the CU's address unit about as much as whole
+    // ones, so operands of one kind stage a whole K step per unit: 128-byte
+    // rows (whole lines) for FP8 x FP8, 64 for FP4 x FP4.  Mixed FP4 x FP8
+    // stages one K half.
+    constexpr bool SAME = (FA == E2M1) == (FB == E2M1);
+    constexpr int SU = SAME ? 2 : 1;
     constexpr int RBA = SU * IA::kh, RBB = SU * IB::kh;  // bytes per row per unit
     constexpr int A_H = BM * RBA, B_H = BN * RBB;        // bytes of one unit of each tile
     constexpr int SLOT = A_H + B_H;
@@ -289,12 +295,15 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     constexpr int FM = BM / 64, FN = BN / 64;              // 32-row fragments per wave
     constexpr int WN = BN / 2;                             // columns of a wave's sub-tile
     constexpr int NM = FM * FN;                            // MFMAs per half
-    // ring slots: eight where they fit in LDS, else four (a power of two that
-    // divides the 8 / SU units of the unrolled group of eight halves)
-    constexpr int NSL = (8 * SLOT + 2 * SCB <= 160 * 1024 && SU == 1) ? 8 : 4;
+    // ring slots: eight, four or two, the most that fit in LDS (a power of
+    // two that divides the 8 / SU units of the unrolled group of eight halves)
+    constexpr int LDS_BYTES = 160 * 1024;
+    constexpr int NSL = (SU == 1 && 8 * SLOT + 2 * SCB <= LDS_BYTES) ? 8 : (4 * SLOT + 2 * SCB <= LDS_BYTES ? 4 : 2);
+    static_assert(NSL * SLOT + 2 * SCB <= LDS_BYTES, "ring must fit in LDS");
+    constexpr int SLOT_MID = NSL >= 4 ? SLOT : 16;
     constexpr int SLOT_HI = NSL == 8 ? SLOT : 16;
     // separate arrays, so the slots are distinct objects to the compiler
-    __shared__ __attribute__((aligned(16))) uint8_t s0[SLOT], s1[SLOT], s2[SLOT], s3[SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t s0[SLOT], s1[SLOT], s2[SLOT_MID], s3[SLOT_MID];
     __shared__ __attribute__((aligned(16))) uint8_t s4[SLOT_HI], s5[SLOT_HI], s6[SLOT_HI], s7[SLOT_HI];
     __shared__ __attribute__((aligned(16))) uint8_t c0[SCB], c1[SCB];
 
@@ -366,9 +375,10 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
         for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
     // Fragment of rows r .. r+31 for K half `sub` of a unit (chunk indexes
-    // within an RB-byte row: FP8 halves are chunks g and 2+g of a 64-byte
-    // row; FP4 half `sub` is chunk 2*sub + g of a 64-byte row, or chunk g of
-    // a 32-byte one).
+    // within an RB-byte row: FP8 half `sub` is chunks 4*sub + g and
+    // 4*sub + 2 + g of a 128-byte row, or g and 2+g of a 64-byte one; FP4
+    // half `sub` is chunk 2*sub + g of a 64-byte row, or chunk g of a 32-byte
+    // one).
     auto frag = [&](const uint8_t* base, int r, int sub, auto info, auto rb) __attribute__((always_inline)) -> v8i {
         using I = decltype(info);
         constexpr int RB = decltype(rb)::value;
@@ -376,8 +386,9 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
             const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, 2 * sub + gq));
             return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
         } else {
-            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, gq));
-            const uint4 y = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, 2 + gq));
+            constexpr int C0 = RB == 128 ? 4 : 0;  // first chunk of half `sub`: C0 * sub
+            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, C0 * sub + gq));
+            const uint4 y = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, C0 * sub + 2 + gq));
             return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
         }
     };
@@ -570,14 +581,17 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     // rows and columns of this wave's sub-tile that exist in C
     const int mlim = (int)min(t.m_end - row_base, (int64_t)(BM / 2));
     const int nlim = (int)min(g.N - col_base, (int64_t)WN);
-    uint8_t* const mine = wave == 0 ? s0 : wave == 1 ? s1 : wave == 2 ? s2 : s3;
+    // staging room per wave: a slot each, or half of slot 0 / 1 with two slots
+    constexpr int CAP = NSL >= 4 ? SLOT : SLOT / 2;
+    uint8_t* const mine = NSL >= 4 ? (wave == 0 ? s0 : wave == 1 ? s1 : wave == 2 ? s2 : s3)
+                                   : (wave < 2 ? s0 : s1) + (wave & 1) * CAP;
     auto store_tile = [&](auto tag) __attribute__((always_inline)) {
         using T = decltype(tag);
         constexpr int PER = 16 / (int)sizeof(T);  // elements per 16-byte chunk
         constexpr int CPR = WN / PER;             // chunks per row
         constexpr int RPI = 64 / CPR;             // rows per wave-wide read
-        constexpr int BR = (32 * WN * (int)sizeof(T) <= SLOT) ? 32 : (16 * WN * (int)sizeof(T) <= SLOT ? 16 : 8);
-        static_assert(BR * WN * (int)sizeof(T) <= SLOT && BR % RPI == 0, "epilogue band");
+        constexpr int BR = (32 * WN * (int)sizeof(T) <= CAP) ? 32 : (16 * WN * (int)sizeof(T) <= CAP ? 16 : 8);
+        static_assert(BR * WN * (int)sizeof(T) <= CAP && BR % RPI == 0, "epilogue band");
         constexpr int RB = BR / 2;                // accumulator registers per band (8 rows <-> 4 registers)
         T* band = reinterpret_cast<T*>(mine);
         T* cw = (T*)g.C + row_base * g.ldc + col_base;
