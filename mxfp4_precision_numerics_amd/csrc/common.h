@@ -80,6 +80,16 @@ __device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Two 16-bit lanes: w + s where w != 0, else 0 (w, s small enough not to wrap).
+__device__ __forceinline__ uint32_t pk_lsum_u16(uint32_t w, uint32_t s2) {
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    const v2u16 x = __builtin_bit_cast(v2u16, w), s = __builtin_bit_cast(v2u16, s2);
+    const v2u16 one = {1, 1};
+    const v2u16 nz = __builtin_elementwise_min(x, one);
+    const v2u16 r = x + nz * s;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // --- conversions -------------------------------------------------------------
 // Two bf16 (one dword, element 0 in the low half) divided by the power of two
 // `scale`, to two FP8 codes placed in the low (hi=false) or high half of `old`.
@@ -209,6 +219,12 @@ __device__ __forceinline__ uint32_t quad4_max_u32(uint32_t v) {
     v = v > o ? v : o;
     o = (uint32_t)__shfl_xor((int)v, 8, 64);
     return v > o ? v : o;
+}
+
+// Same on two 16-bit lanes at once.
+__device__ __forceinline__ uint32_t quad4_max_pk16(uint32_t v) {
+    v = pk_max_u16(v, (uint32_t)__shfl_xor((int)v, 4, 64));
+    return pk_max_u16(v, (uint32_t)__shfl_xor((int)v, 8, 64));
 }
 
 // 4x4 byte transpose: r[i] holds bytes (row i, cols 0..3); on return r[j]

@@ -122,9 +122,10 @@ hipError_t launch_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const 
 //  lanes that differ in lane bits 2-3.
 // Each element is m * 2^(s-127) with m an E2M1 value; its exponent is that of
 // m plus s - 127, so the block exponent is an integer max and every element
-// divided by the block scale is m * 2^(s-127-e), formed with ldexp (exact
-// where it can reach E4M3's range), saturated at 448 and rounded to nearest
-// even by the converter.
+// divided by the block scale is m * 2^(s-127-e), formed with ldexp from a
+// byte table of 2|m| (exact where it can reach E4M3's range) and rounded to
+// nearest even by the converter.  The block exponent puts the largest
+// magnitude at 256 or 384, so nothing saturates.
 // LDS rows hold 32 dwords of codes; dword index bits 2-4 are XOR-ed with the
 // row's bits 3-5, which halves the column reads' bank conflicts to 2-way.
 // ---------------------------------------------------------------------------
@@ -162,55 +163,66 @@ __global__ void __launch_bounds__(256) k_fp4_row_to_fp8_col(const uint8_t* __res
     }
     __syncthreads();
     const int g = lane >> 2;
+    // byte tables indexed by an E2M1 magnitude code k (0..7), entries 0..3 in
+    // the low word: 2|m| (0, 1, 2, 3, 4, 6, 8, 12) and floor(log2 2|m|) + 1
+    // (0 for zero)
+    constexpr uint32_t V_LO = 0x03020100u, V_HI = 0x0C080604u;
+    constexpr uint32_t L_LO = 0x02020100u, L_HI = 0x04040303u;
 #pragma unroll 1
     for (int h = 0; h < 2; ++h) {
         const int cg = 16 * h + 4 * w + (lane & 3);  // 8-column group of the tile, 0..31
-        uint32_t d[8];
-        int sc[8];
+        // Per source row i (one token): 2|m| of columns 0,2,4,6 (vl) and
+        // 1,3,5,7 (vh) as bytes, their sign bits (bit 3 of each byte), and
+        // s - 128.  An element's floor(log2 |v|) + 129 is L(k) + s for k != 0,
+        // so the block exponent per column is a max over rows of L + s,
+        // kept on 16-bit lanes: m0 = columns (0, 4), m1 = (2, 6), m2 = (1, 5),
+        // m3 = (3, 7); 0 means no non-zero element.
+        uint32_t vl[8], vh[8], sl[8], sh[8];
+        int a[8];
+        uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
         bool bad = false;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * g + i;
-            d[i] = codes[r * 32 + fc_swz(r, cg)];
-            sc[i] = scales[r * 8 + (cg >> 2)];
-            bad |= sc[i] == 0xFF;
+            const uint32_t dd = codes[r * 32 + fc_swz(r, cg)];
+            const uint32_t sc = scales[r * 8 + (cg >> 2)];
+            bad |= sc == 0xFFu;
+            const uint32_t klo = dd & 0x07070707u, khi = (dd >> 4) & 0x07070707u;
+            sl[i] = dd & 0x08080808u;
+            sh[i] = (dd >> 4) & 0x08080808u;
+            vl[i] = __builtin_amdgcn_perm(V_HI, V_LO, klo);
+            vh[i] = __builtin_amdgcn_perm(V_HI, V_LO, khi);
+            const uint32_t ll = __builtin_amdgcn_perm(L_HI, L_LO, klo), lh = __builtin_amdgcn_perm(L_HI, L_LO, khi);
+            const uint32_t s2 = sc * 0x00010001u;
+            m0 = pk_max_u16(m0, pk_lsum_u16(ll & 0x00FF00FFu, s2));
+            m1 = pk_max_u16(m1, pk_lsum_u16((ll >> 8) & 0x00FF00FFu, s2));
+            m2 = pk_max_u16(m2, pk_lsum_u16(lh & 0x00FF00FFu, s2));
+            m3 = pk_max_u16(m3, pk_lsum_u16((lh >> 8) & 0x00FF00FFu, s2));
+            a[i] = (int)sc - 128;
         }
         bad = quad4_max_u32(bad ? 1u : 0u) != 0u;  // the block's 32 tokens
-        // Block exponent per column.  For a non-zero E2M1 magnitude code k
-        // (1..7: 0.5, 1, 1.5, 2, 3, 4, 6) floor(log2 |m|) + 1 = k >> 1, so an
-        // element's floor(log2 |v|) is (k >> 1) + s - 128; the max over the
-        // block is kept as (k >> 1) + s + 1 (0: no non-zero element).
-        uint32_t emax[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t m = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t k = (d[i] >> (4 * j)) & 7u;
-                const uint32_t E = k != 0u ? (k >> 1) + (uint32_t)sc[i] + 1u : 0u;
-                m = m > E ? m : E;
-            }
-            emax[j] = quad4_max_u32(m);
-        }
+        m0 = quad4_max_pk16(m0);
+        m1 = quad4_max_pk16(m1);
+        m2 = quad4_max_pk16(m2);
+        m3 = quad4_max_pk16(m3);
+        const uint32_t em[8] = {m0 & 0xFFFFu, m2 & 0xFFFFu, m1 & 0xFFFFu, m3 & 0xFFFFu,
+                                m0 >> 16,     m2 >> 16,     m1 >> 16,     m3 >> 16};
         const int64_t c0 = tc + 8 * cg;
         const bool live = tr + 8 * g < rows && c0 < cols;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            int e = emax[j] == 0u ? -127 : (int)emax[j] - 137;  // floor(log2 amax) - 8 (E4M3 emax)
-            e = e < -127 ? -127 : (e > 127 ? 127 : e);
+            // floor(log2 amax) - 8 (E4M3 emax), clamped below at -127 (also
+            // the all-zero block); it never exceeds 121
+            const int e = max((int)em[j] - 137, -127);
+            const int b = j >> 1;  // byte of column j in vl / vh
             float y[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t n = (d[i] >> (4 * j)) & 0xFu;
-                const uint32_t k = n & 7u;
-                // 2|m| = 0, 1, 2, 3 for k < 4, else (2 + (k & 1)) << ((k >> 1) - 1)
-                const uint32_t hiv = ((2u + (k & 1u)) << ((k >> 1) & 3u)) >> 1;
-                const uint32_t two_m = k < 4u ? k : hiv;
-                // |v| / 2^e = 2|m| * 2^(s - 128 - e): exact where it can reach
-                // E4M3's range (ldexp of a 2-bit integer), zero stays zero
-                float v = __builtin_amdgcn_ldexpf((float)two_m, sc[i] - 128 - e);
-                v = v < 448.0f ? v : 448.0f;  // saturate
-                y[i] = as_float(as_uint(v) | ((n & 8u) << 28));
+                const uint32_t vb = (j & 1) ? vh[i] : vl[i], sb = (j & 1) ? sh[i] : sl[i];
+                // |v| / 2^e = 2|m| * 2^(s - 128 - e), exact wherever it can
+                // reach E4M3's range and at most 384 (no saturation)
+                const float v = __builtin_amdgcn_ldexpf((float)((vb >> (8 * b)) & 0xFFu), a[i] - e);
+                y[i] = as_float(as_uint(v) | ((sb << (28 - 8 * b)) & 0x80000000u));
             }
             uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
             lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
