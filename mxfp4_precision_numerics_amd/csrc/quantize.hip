@@ -331,7 +331,7 @@ __global__ void __launch_bounds__(64) k_pt_history(float* history, int hist_len,
 // codes and scales are written contiguously.
 // ---------------------------------------------------------------------------
 constexpr int MXR_THREADS = 256;
-constexpr int MXR_VEC_PER_THREAD = 4;
+constexpr int MXR_VEC_PER_THREAD = 2;
 
 template <int F, int SRC, bool DENSE>
 __global__ void __launch_bounds__(MXR_THREADS) k_mx_row(const void* __restrict__ x, int64_t nvec, int64_t vpr,

@@ -23,7 +23,7 @@
 namespace mxq {
 
 constexpr int RP_THREADS = 256;
-constexpr int RP_PER_THREAD = 4;
+constexpr int RP_PER_THREAD = 1;  // more waves in flight hide the index -> data latency chain best
 
 // E4M3 codes of 8 E2M1 codes (one dword, element 0 in the low nibble) through
 // the table (tlo: entries 0..3, thi: 4..7); two dwords of 4 codes each.
