@@ -80,13 +80,13 @@ __device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// Two 16-bit lanes: w + s where w != 0, else 0 (w, s small enough not to wrap).
+// Two 16-bit lanes: w + s where w != 0, else 0, for w <= 63 and w + s below
+// 1024: min(w + s, w << 10) (packed adds, shifts and mins only).
 __device__ __forceinline__ uint32_t pk_lsum_u16(uint32_t w, uint32_t s2) {
     typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
     const v2u16 x = __builtin_bit_cast(v2u16, w), s = __builtin_bit_cast(v2u16, s2);
-    const v2u16 one = {1, 1};
-    const v2u16 nz = __builtin_elementwise_min(x, one);
-    const v2u16 r = x + nz * s;
+    const v2u16 ten = {10, 10};
+    const v2u16 r = __builtin_elementwise_min(x + s, x << ten);
     return __builtin_bit_cast(uint32_t, r);
 }
 
@@ -221,10 +221,12 @@ __device__ __forceinline__ uint32_t quad4_max_u32(uint32_t v) {
     return v > o ? v : o;
 }
 
-// Same on two 16-bit lanes at once.
+// Max over lanes l, l^4, l^8, l^12 of two 16-bit lanes at once.  Those four
+// lanes share a DPP row of 16, so rotations of the row by 4 and by 8 reach
+// them (no LDS crossbar).
 __device__ __forceinline__ uint32_t quad4_max_pk16(uint32_t v) {
-    v = pk_max_u16(v, (uint32_t)__shfl_xor((int)v, 4, 64));
-    return pk_max_u16(v, (uint32_t)__shfl_xor((int)v, 8, 64));
+    v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+    return pk_max_u16(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
 }
 
 // 4x4 byte transpose: r[i] holds bytes (row i, cols 0..3); on return r[j]

@@ -111,7 +111,9 @@ hipError_t launch_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const 
 // contracts over the tokens) reads FP8 blocks along the tokens.  Reading:
 // exact dequantization, then MX block-32 E4M3 along the new rows.
 //
-// A block of 256 threads owns a tile of 128 source rows x 256 source columns.
+// A persistent block of 256 threads walks tiles of 128 source rows x 256
+// source columns with the grid's stride; the next tile's loads are in flight
+// while the current one is converted from LDS.
 //  Row phase: wave w, step it reads source row 16*it + 4*w + l/16, 16 lanes
 //  per row, 16 codes (8 bytes) per lane: whole 128-byte lines.  Codes go to
 //  LDS as they are (4 bits each); the row's 8 scale bytes too.
@@ -130,21 +132,23 @@ hipError_t launch_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const 
 // row's bits 3-5, which halves the column reads' bank conflicts to 2-way.
 // ---------------------------------------------------------------------------
 constexpr int FC_ROWS = 128, FC_COLS = 256;
+constexpr int FC_GRID = 512;  // persistent blocks (two per CU); each walks tiles with the grid's stride
 
 __device__ __forceinline__ int fc_swz(int r, int dw) { return dw ^ (((r >> 3) & 7) << 2); }
 
 __global__ void __launch_bounds__(256) k_fp4_row_to_fp8_col(const uint8_t* __restrict__ q4,
                                                             const uint8_t* __restrict__ s4, int64_t rows,
-                                                            int64_t cols, uint8_t* __restrict__ q8,
-                                                            uint8_t* __restrict__ s8) {
+                                                            int64_t cols, int64_t ntc, int64_t ntiles,
+                                                            uint8_t* __restrict__ q8, uint8_t* __restrict__ s8) {
     __shared__ __attribute__((aligned(16))) uint32_t codes[FC_ROWS * 32];
     __shared__ uint8_t scales[FC_ROWS * 8];
-    const int64_t tr = (int64_t)blockIdx.y * FC_ROWS, tc = (int64_t)blockIdx.x * FC_COLS;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int ch = lane & 15;
-    {
-        uint2 c[8];
-        uint8_t sb[8];
+    // the row phase's loads of tile t (zeros outside the tensor)
+    uint2 c[8];
+    uint32_t sb[8];
+    auto load_tile = [&](int64_t t) __attribute__((always_inline)) {
+        const int64_t tr = (t / ntc) * FC_ROWS, tc = (t % ntc) * FC_COLS;
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
             const int r = 16 * it + 4 * w + (lane >> 4);
@@ -154,93 +158,102 @@ __global__ void __launch_bounds__(256) k_fp4_row_to_fp8_col(const uint8_t* __res
             if (rok && tc + 16 * ch < cols) c[it] = ld_nt8(q4 + (tr + r) * (cols / 2) + tc / 2 + 8 * ch);
             if (rok && ch < 8 && tc + 32 * ch < cols) sb[it] = s4[(tr + r) * (cols / 32) + tc / 32 + ch];
         }
+    };
+    int64_t t = blockIdx.x;
+    if (t < ntiles) load_tile(t);
+    for (; t < ntiles; t += gridDim.x) {
+        const int64_t tr = (t / ntc) * FC_ROWS, tc = (t % ntc) * FC_COLS;
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
             const int r = 16 * it + 4 * w + (lane >> 4);
             *reinterpret_cast<uint2*>(&codes[r * 32 + fc_swz(r, 2 * ch)]) = c[it];
-            if (ch < 8) scales[r * 8 + ch] = sb[it];
+            if (ch < 8) scales[r * 8 + ch] = (uint8_t)sb[it];
         }
-    }
-    __syncthreads();
-    const int g = lane >> 2;
-    // byte tables indexed by an E2M1 magnitude code k (0..7), entries 0..3 in
-    // the low word: 2|m| (0, 1, 2, 3, 4, 6, 8, 12) and floor(log2 2|m|) + 1
-    // (0 for zero)
-    constexpr uint32_t V_LO = 0x03020100u, V_HI = 0x0C080604u;
-    constexpr uint32_t L_LO = 0x02020100u, L_HI = 0x04040303u;
+        __syncthreads();
+        // the next tile's loads are in flight during this tile's column phase
+        if (t + gridDim.x < ntiles) load_tile(t + gridDim.x);
+        const int g = lane >> 2;
+        // byte tables indexed by an E2M1 magnitude code k (0..7), entries 0..3 in
+        // the low word: 2|m| (0, 1, 2, 3, 4, 6, 8, 12) and floor(log2 2|m|) + 1
+        // (0 for zero)
+        constexpr uint32_t V_LO = 0x03020100u, V_HI = 0x0C080604u;
+        constexpr uint32_t L_LO = 0x02020100u, L_HI = 0x04040303u;
 #pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
-        const int cg = 16 * h + 4 * w + (lane & 3);  // 8-column group of the tile, 0..31
-        // Per source row i (one token): 2|m| of columns 0,2,4,6 (vl) and
-        // 1,3,5,7 (vh) as bytes, their sign bits (bit 3 of each byte), and
-        // s - 128.  An element's floor(log2 |v|) + 129 is L(k) + s for k != 0,
-        // so the block exponent per column is a max over rows of L + s,
-        // kept on 16-bit lanes: m0 = columns (0, 4), m1 = (2, 6), m2 = (1, 5),
-        // m3 = (3, 7); 0 means no non-zero element.
-        uint32_t vl[8], vh[8], sl[8], sh[8];
-        int a[8];
-        uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
-        bool bad = false;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 8 * g + i;
-            const uint32_t dd = codes[r * 32 + fc_swz(r, cg)];
-            const uint32_t sc = scales[r * 8 + (cg >> 2)];
-            bad |= sc == 0xFFu;
-            const uint32_t klo = dd & 0x07070707u, khi = (dd >> 4) & 0x07070707u;
-            sl[i] = dd & 0x08080808u;
-            sh[i] = (dd >> 4) & 0x08080808u;
-            vl[i] = __builtin_amdgcn_perm(V_HI, V_LO, klo);
-            vh[i] = __builtin_amdgcn_perm(V_HI, V_LO, khi);
-            const uint32_t ll = __builtin_amdgcn_perm(L_HI, L_LO, klo), lh = __builtin_amdgcn_perm(L_HI, L_LO, khi);
-            const uint32_t s2 = sc * 0x00010001u;
-            m0 = pk_max_u16(m0, pk_lsum_u16(ll & 0x00FF00FFu, s2));
-            m1 = pk_max_u16(m1, pk_lsum_u16((ll >> 8) & 0x00FF00FFu, s2));
-            m2 = pk_max_u16(m2, pk_lsum_u16(lh & 0x00FF00FFu, s2));
-            m3 = pk_max_u16(m3, pk_lsum_u16((lh >> 8) & 0x00FF00FFu, s2));
-            a[i] = (int)sc - 128;
-        }
-        bad = quad4_max_u32(bad ? 1u : 0u) != 0u;  // the block's 32 tokens
-        m0 = quad4_max_pk16(m0);
-        m1 = quad4_max_pk16(m1);
-        m2 = quad4_max_pk16(m2);
-        m3 = quad4_max_pk16(m3);
-        const uint32_t em[8] = {m0 & 0xFFFFu, m2 & 0xFFFFu, m1 & 0xFFFFu, m3 & 0xFFFFu,
-                                m0 >> 16,     m2 >> 16,     m1 >> 16,     m3 >> 16};
-        const int64_t c0 = tc + 8 * cg;
-        const bool live = tr + 8 * g < rows && c0 < cols;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            // floor(log2 amax) - 8 (E4M3 emax), clamped below at -127 (also
-            // the all-zero block); it never exceeds 121
-            const int e = max((int)em[j] - 137, -127);
-            const int b = j >> 1;  // byte of column j in vl / vh
-            float y[8];
+        for (int h = 0; h < 2; ++h) {
+            const int cg = 16 * h + 4 * w + (lane & 3);  // 8-column group of the tile, 0..31
+            // Per source row i (one token): 2|m| of columns 0,2,4,6 (vl) and
+            // 1,3,5,7 (vh) as bytes, their sign bits (bit 3 of each byte), and
+            // s - 128.  An element's floor(log2 |v|) + 129 is L(k) + s for k != 0,
+            // so the block exponent per column is a max over rows of L + s,
+            // kept on 16-bit lanes: m0 = columns (0, 4), m1 = (2, 6), m2 = (1, 5),
+            // m3 = (3, 7); 0 means no non-zero element.
+            uint32_t vl[8], vh[8], sl[8], sh[8];
+            int a[8];
+            uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+            bool bad = false;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t vb = (j & 1) ? vh[i] : vl[i], sb = (j & 1) ? sh[i] : sl[i];
-                // |v| / 2^e = 2|m| * 2^(s - 128 - e), exact wherever it can
-                // reach E4M3's range and at most 384 (no saturation)
-                const float v = __builtin_amdgcn_ldexpf((float)((vb >> (8 * b)) & 0xFFu), a[i] - e);
-                y[i] = as_float(as_uint(v) | ((sb << (28 - 8 * b)) & 0x80000000u));
+                const int r = 8 * g + i;
+                const uint32_t dd = codes[r * 32 + fc_swz(r, cg)];
+                const uint32_t sc = scales[r * 8 + (cg >> 2)];
+                bad |= sc == 0xFFu;
+                const uint32_t klo = dd & 0x07070707u, khi = (dd >> 4) & 0x07070707u;
+                sl[i] = dd & 0x08080808u;
+                sh[i] = (dd >> 4) & 0x08080808u;
+                vl[i] = __builtin_amdgcn_perm(V_HI, V_LO, klo);
+                vh[i] = __builtin_amdgcn_perm(V_HI, V_LO, khi);
+                const uint32_t ll = __builtin_amdgcn_perm(L_HI, L_LO, klo), lh = __builtin_amdgcn_perm(L_HI, L_LO, khi);
+                const uint32_t s2 = sc * 0x00010001u;
+                m0 = pk_max_u16(m0, pk_lsum_u16(ll & 0x00FF00FFu, s2));
+                m1 = pk_max_u16(m1, pk_lsum_u16((ll >> 8) & 0x00FF00FFu, s2));
+                m2 = pk_max_u16(m2, pk_lsum_u16(lh & 0x00FF00FFu, s2));
+                m3 = pk_max_u16(m3, pk_lsum_u16((lh >> 8) & 0x00FF00FFu, s2));
+                a[i] = (int)sc - 128;
             }
-            uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-            lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
-            uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-            hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
-            if (bad) { lo = 0x7F7F7F7Fu; hi = 0x7F7F7F7Fu; }
-            if (live) {
-                st_nt8(q8 + (c0 + j) * rows + tr + 8 * g, make_uint2(lo, hi));
-                if ((g & 3) == 0) s8[(c0 + j) * (rows / 32) + (tr + 8 * g) / 32] = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
+            bad = quad4_max_pk16(bad ? 1u : 0u) != 0u;  // the block's 32 tokens
+            m0 = quad4_max_pk16(m0);
+            m1 = quad4_max_pk16(m1);
+            m2 = quad4_max_pk16(m2);
+            m3 = quad4_max_pk16(m3);
+            const uint32_t em[8] = {m0 & 0xFFFFu, m2 & 0xFFFFu, m1 & 0xFFFFu, m3 & 0xFFFFu,
+                                    m0 >> 16,     m2 >> 16,     m1 >> 16,     m3 >> 16};
+            const int64_t c0 = tc + 8 * cg;
+            const bool live = tr + 8 * g < rows && c0 < cols;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // floor(log2 amax) - 8 (E4M3 emax), clamped below at -127 (also
+                // the all-zero block); it never exceeds 121
+                const int e = max((int)em[j] - 137, -127);
+                const int b = j >> 1;  // byte of column j in vl / vh
+                float y[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t vb = (j & 1) ? vh[i] : vl[i], sb = (j & 1) ? sh[i] : sl[i];
+                    // |v| / 2^e = 2|m| * 2^(s - 128 - e), exact wherever it can
+                    // reach E4M3's range and at most 384 (no saturation)
+                    const float v = __builtin_amdgcn_ldexpf((float)((vb >> (8 * b)) & 0xFFu), a[i] - e);
+                    y[i] = as_float(as_uint(v) | ((sb << (28 - 8 * b)) & 0x80000000u));
+                }
+                uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+                lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
+                uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+                hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
+                if (bad) { lo = 0x7F7F7F7Fu; hi = 0x7F7F7F7Fu; }
+                if (live) {
+                    st_nt8(q8 + (c0 + j) * rows + tr + 8 * g, make_uint2(lo, hi));
+                    if ((g & 3) == 0) s8[(c0 + j) * (rows / 32) + (tr + 8 * g) / 32] = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
+                }
             }
         }
+        __syncthreads();  // LDS is free for the next tile
     }
 }
 
 hipError_t launch_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, int64_t cols, uint8_t* q8,
                                      uint8_t* s8, hipStream_t st) {
-    const dim3 grid((unsigned)((cols + FC_COLS - 1) / FC_COLS), (unsigned)((rows + FC_ROWS - 1) / FC_ROWS));
-    hipLaunchKernelGGL(k_fp4_row_to_fp8_col, grid, dim3(256), 0, st, q4, s4, rows, cols, q8, s8);
+    const int64_t ntc = (cols + FC_COLS - 1) / FC_COLS, ntiles = ntc * ((rows + FC_ROWS - 1) / FC_ROWS);
+    const unsigned grid = (unsigned)(ntiles < FC_GRID ? ntiles : FC_GRID);
+    hipLaunchKernelGGL(k_fp4_row_to_fp8_col, dim3(grid), dim3(256), 0, st, q4, s4, rows, cols, ntc, ntiles, q8, s8);
     return hipGetLastError();
 }
 
