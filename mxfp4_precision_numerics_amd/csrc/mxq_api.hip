@@ -72,7 +72,7 @@ int mxq_quantize_mx(const void* x, int src, int64_t rows, int64_t cols, int64_t 
     if (cols % 32 != 0 || ld_x < cols) return MXQ_ERR_SHAPE;
     if (q_col && rows % 32 != 0) return MXQ_ERR_SHAPE;
     if (q_col && (rows + 127) / 128 > MAX_GRID_Y) return MXQ_ERR_SHAPE;
-    if (!q_col && rows * (cols / 8) / 1024 + 1 > MAX_GRID_X) return MXQ_ERR_SHAPE;
+    if (!q_col && rows * (cols / 8) / 512 + 1 > MAX_GRID_X) return MXQ_ERR_SHAPE;  // 512 vectors per block
     const int64_t esz = src == MXQ_SRC_BF16 ? 2 : 4;
     if (!aligned16(x) || (ld_x * esz) % 16 != 0) return MXQ_ERR_ALIGN;
     if ((q_row && !aligned16(q_row)) || (s_row && !aligned16(s_row)) || (q_col && !aligned16(q_col)) ||
@@ -89,7 +89,7 @@ int mxq_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const int32_t* g
     if (!q4 || !s4 || !q8 || !s8) return MXQ_ERR_NULL;
     if (cols % 128 != 0) return MXQ_ERR_SHAPE;
     if (!gather_idx && rows > src_rows) return MXQ_ERR_SHAPE;
-    if (rows * (cols / 128) * 8 / 256 + 1 > MAX_GRID_X) return MXQ_ERR_SHAPE;
+    if (rows * (cols / 128) * 4 / 256 + 1 > MAX_GRID_X) return MXQ_ERR_SHAPE;  // one 32-block per lane
     if (!aligned16(q4) || !aligned16(s4) || !aligned16(q8) || !aligned16(s8) ||
         (gather_idx && !aligned4(gather_idx)))
         return MXQ_ERR_ALIGN;

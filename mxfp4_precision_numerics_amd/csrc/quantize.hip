@@ -227,12 +227,31 @@ __device__ __forceinline__ uint2 cast8_pt(const uint32_t (&u)[8], float scale, b
 // COL: also the transposed codes (rows % 16 == 0).  Blocks walk the ntiles
 // tiles (ntc per tile row) with a stride of the grid, loading the next tile
 // while casting the current one.
+// Tiles are TT rows x PT_TC(SRC) columns: 256 columns for bf16 input, so
+// that each row's loads cover 512 contiguous bytes and each row-code store
+// 256 (128-column tiles, 256-byte reads, measured 4.0 TB/s on a row-only
+// cast against 6.5 TB/s for the MX quantizer's contiguous stream).  In the
+// row phase LPR = cols/8 lanes share a tile row; in the column phase (one
+// pass per 128 columns) lane l of wave w takes rows 8*(l/4) .. +7 of column
+// group 16*pass + 4*w + l%4, so the 16 lanes of a column group write one
+// 128-byte line of the transposed output.  LDS rows are chunks of 8 codes;
+// the chunk index's bits 2.. are XOR-ed with the row's bits 3.., which keeps
+// the column phase's reads free of bank conflicts.
+template <int SRC> constexpr int pt_tc() { return SRC == 1 ? 256 : 128; }
+template <int TC> __device__ __forceinline__ int pt_swz(int r, int c) {
+    return c ^ (((r >> 3) & (TC / 32 - 1)) << 2);
+}
+
 template <int F, int SRC, bool DELAYED, bool COL>
 __global__ void __launch_bounds__(256) k_pt_cast(const void* __restrict__ x, int64_t rows, int64_t cols,
                                                  int64_t ld, int64_t ntc, int64_t ntiles, unsigned int* amax_acc,
                                                  float* scale_out, float* scale_inv_out,
                                                  uint8_t* __restrict__ q_row, uint8_t* __restrict__ q_col) {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[COL ? TT * TT : 16];
+    constexpr int TC = pt_tc<SRC>();
+    constexpr int LPR = TC / 8;           // lanes per tile row in the row phase
+    constexpr int RPS = 64 / LPR;         // rows per wave and step
+    constexpr int NSTEP = TT / (4 * RPS); // row-phase steps
+    __shared__ __attribute__((aligned(16))) uint8_t tile[COL ? TT * TC : 16];
     float scale;
     if (DELAYED) {
         scale = scale_out[0];
@@ -244,61 +263,66 @@ __global__ void __launch_bounds__(256) k_pt_cast(const void* __restrict__ x, int
         }
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int ch = lane & 15;  // row phase: chunk of 8 columns
-    auto load_tile = [&](int64_t t, uint32_t (&u)[8][8]) __attribute__((always_inline)) {
-        const int64_t tr = (t / ntc) * TT, tc = (t % ntc) * TT;
+    const int ch = lane % LPR;  // row phase: chunk of 8 columns
+    auto row_of = [&](int it) __attribute__((always_inline)) { return 4 * RPS * it + RPS * w + lane / LPR; };
+    auto load_tile = [&](int64_t t, uint32_t (&u)[NSTEP][8]) __attribute__((always_inline)) {
+        const int64_t tr = (t / ntc) * TT, tc = (t % ntc) * TC;
         const bool cok = tc + 8 * ch < cols;  // cols % 16 == 0: a chunk is all-in or all-out
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int r = 16 * it + 4 * w + (lane >> 4);
+        for (int it = 0; it < NSTEP; ++it) {
+            const int r = row_of(it);
             load_raw8<SRC>(x, (tr + r) * ld + tc + 8 * ch, cok && tr + r < rows, u[it]);
         }
     };
     uint32_t m = 0;
-    uint32_t u[8][8];
+    uint32_t u[NSTEP][8];
     int64_t t = blockIdx.x;
     if (t < ntiles) load_tile(t, u);
     for (; t < ntiles; t += gridDim.x) {
-        uint32_t un[8][8];
+        uint32_t un[NSTEP][8];
         if (t + gridDim.x < ntiles) load_tile(t + gridDim.x, un);
-        const int64_t tr = (t / ntc) * TT, tc = (t % ntc) * TT;
+        const int64_t tr = (t / ntc) * TT, tc = (t % ntc) * TC;
         const bool cok = tc + 8 * ch < cols;
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int r = 16 * it + 4 * w + (lane >> 4);
+        for (int it = 0; it < NSTEP; ++it) {
+            const int r = row_of(it);
             const uint32_t a = amax8<SRC>(u[it]);
             if (DELAYED) m = m > a ? m : a;
             const uint2 c = cast8_pt<F, SRC>(u[it], scale, a > 0x7F800000u);
             if (q_row && cok && tr + r < rows) st_nt8(q_row + (tr + r) * cols + tc + 8 * ch, c);
-            if constexpr (COL) *reinterpret_cast<uint2*>(tile + r * TT + 8 * chunk_swz(r, ch)) = c;
+            if constexpr (COL) *reinterpret_cast<uint2*>(tile + r * TC + 8 * pt_swz<TC>(r, ch)) = c;
         }
         if constexpr (COL) {
             __syncthreads();
-            const int g = lane >> 2, cg = 4 * w + (lane & 3);  // 8-row group, 8-column group
-            uint32_t lo[8], hi[8];                              // patch row i: columns 0..3, 4..7
+            const int g = lane >> 2;  // 8-row group
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int r = 8 * g + i;
-                const uint2 v = *reinterpret_cast<const uint2*>(tile + r * TT + 8 * chunk_swz(r, cg));
-                lo[i] = v.x;
-                hi[i] = v.y;
-            }
-            __syncthreads();  // the tile is free for the next round
-            if (tr + 8 * g < rows && tc + 8 * cg < cols) {  // rows % 16 == 0: a patch is all-in or all-out
-                transpose4x4_bytes(lo[0], lo[1], lo[2], lo[3]);  // cols 0..3, rows 0..3
-                transpose4x4_bytes(lo[4], lo[5], lo[6], lo[7]);  // cols 0..3, rows 4..7
-                transpose4x4_bytes(hi[0], hi[1], hi[2], hi[3]);  // cols 4..7, rows 0..3
-                transpose4x4_bytes(hi[4], hi[5], hi[6], hi[7]);  // cols 4..7, rows 4..7
-                uint8_t* const dst = q_col + (tc + 8 * cg) * rows + tr + 8 * g;
+            for (int pass = 0; pass < TC / 128; ++pass) {
+                const int cg = 16 * pass + 4 * w + (lane & 3);  // 8-column group
+                uint32_t lo[8], hi[8];                          // patch row i: columns 0..3, 4..7
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    st_nt8(dst + j * rows, make_uint2(lo[j], lo[4 + j]));
-                    st_nt8(dst + (4 + j) * rows, make_uint2(hi[j], hi[4 + j]));
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 8 * g + i;
+                    const uint2 v = *reinterpret_cast<const uint2*>(tile + r * TC + 8 * pt_swz<TC>(r, cg));
+                    lo[i] = v.x;
+                    hi[i] = v.y;
+                }
+                if (tr + 8 * g < rows && tc + 8 * cg < cols) {  // rows % 16 == 0: a patch is all-in or all-out
+                    transpose4x4_bytes(lo[0], lo[1], lo[2], lo[3]);  // cols 0..3, rows 0..3
+                    transpose4x4_bytes(lo[4], lo[5], lo[6], lo[7]);  // cols 0..3, rows 4..7
+                    transpose4x4_bytes(hi[0], hi[1], hi[2], hi[3]);  // cols 4..7, rows 0..3
+                    transpose4x4_bytes(hi[4], hi[5], hi[6], hi[7]);  // cols 4..7, rows 4..7
+                    uint8_t* const dst = q_col + (tc + 8 * cg) * rows + tr + 8 * g;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        st_nt8(dst + j * rows, make_uint2(lo[j], lo[4 + j]));
+                        st_nt8(dst + (4 + j) * rows, make_uint2(hi[j], hi[4 + j]));
+                    }
                 }
             }
+            __syncthreads();  // the tile is free for the next round
         }
 #pragma unroll
-        for (int it = 0; it < 8; ++it)
+        for (int it = 0; it < NSTEP; ++it)
 #pragma unroll
             for (int k = 0; k < 8; ++k) u[it][k] = un[it][k];
     }
@@ -541,7 +565,8 @@ static hipError_t launch_pt(const void* x, int64_t rows, int64_t cols, int64_t l
                             uint8_t* q_col, hipStream_t st) {
     unsigned int* acc = reinterpret_cast<unsigned int*>(amax_out);
     hipLaunchKernelGGL((k_pt_prologue<F>), dim3(1), dim3(64), 0, st, history, hist_len, acc, scale_out, scale_inv_out);
-    const int64_t ntc = (cols + TT - 1) / TT, ntiles = ntc * ((rows + TT - 1) / TT);
+    constexpr int TC = pt_tc<SRC>();
+    const int64_t ntc = (cols + TC - 1) / TC, ntiles = ntc * ((rows + TT - 1) / TT);
     const dim3 grid((unsigned)(ntiles < PERSIST_BLOCKS ? ntiles : PERSIST_BLOCKS));
     if (hist_len > 0) {
         if (q_col)
