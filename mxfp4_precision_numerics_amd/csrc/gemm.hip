@@ -20,12 +20,12 @@
 // 32-bit scale operand is used.
 //
 // Pipeline.  K runs in halves of 64 elements (one MFMA deep), staged in
-// ring units of one K step (two halves) for operands of one kind (FP8 x FP8:
-// whole 128-byte lines per row; FP4 x FP4: 64 bytes) or of one half for
-// mixed FP4 x FP8.  A block (4 waves, 2 x 2 over the tile) keeps a ring of
-// NSL LDS slots of one unit of the A and B tiles each (two for the 256 x 256
-// FP8 tile, four or eight where they fit), and two slots of scale dwords (a
-// group of four K steps each).  In half j every wave:
+// ring units of whole 128-byte lines per row for operands of one kind (one
+// K step for FP8 x FP8, two for FP4 x FP4) or of one half for mixed
+// FP4 x FP8.  A block (4 waves, 2 x 2 over the tile) keeps a ring of
+// NSL LDS slots of one unit of the A and B tiles each (two for 256 x 256
+// FP8 tiles and for FP4 x FP4, four or eight where they fit), and two slots
+// of scale dwords (a group of four K steps each).  In half j every wave:
 //   * runs the half's MFMAs from fragments already in registers,
 //   * reads the next half's fragments (landed) into the other register set,
 //     interleaved with the MFMAs,
@@ -283,11 +283,11 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     using IB = OpInfo<FB>;
     // Ring unit: SU K halves.  Copies fetch RB contiguous bytes per row, and
     // partial-line copies cost the CU's address unit about as much as whole
-    // ones, so operands of one kind stage a whole K step per unit: 128-byte
-    // rows (whole lines) for FP8 x FP8, 64 for FP4 x FP4.  Mixed FP4 x FP8
+    // ones, so operands of one kind stage whole 128-byte lines per row and
+    // unit: one K step for FP8 x FP8, two for FP4 x FP4.  Mixed FP4 x FP8
     // stages one K half.
     constexpr bool SAME = (FA == E2M1) == (FB == E2M1);
-    constexpr int SU = SAME ? 2 : 1;
+    constexpr int SU = SAME ? (FA == E2M1 ? 4 : 2) : 1;
     constexpr int RBA = SU * IA::kh, RBB = SU * IB::kh;  // bytes per row per unit
     constexpr int A_H = BM * RBA, B_H = BN * RBB;        // bytes of one unit of each tile
     constexpr int SLOT = A_H + B_H;
@@ -298,7 +298,8 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     // ring slots: eight, four or two, the most that fit in LDS (a power of
     // two that divides the 8 / SU units of the unrolled group of eight halves)
     constexpr int LDS_BYTES = 160 * 1024;
-    constexpr int NSL = (SU == 1 && 8 * SLOT + 2 * SCB <= LDS_BYTES) ? 8 : (4 * SLOT + 2 * SCB <= LDS_BYTES ? 4 : 2);
+    constexpr int NSL = (SU == 1 && 8 * SLOT + 2 * SCB <= LDS_BYTES) ? 8
+                        : (SU <= 2 && 4 * SLOT + 2 * SCB <= LDS_BYTES ? 4 : 2);
     static_assert(NSL * SLOT + 2 * SCB <= LDS_BYTES, "ring must fit in LDS");
     constexpr int SLOT_MID = NSL >= 4 ? SLOT : 16;
     constexpr int SLOT_HI = NSL == 8 ? SLOT : 16;
@@ -377,8 +378,8 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     // Fragment of rows r .. r+31 for K half `sub` of a unit (chunk indexes
     // within an RB-byte row: FP8 half `sub` is chunks 4*sub + g and
     // 4*sub + 2 + g of a 128-byte row, or g and 2+g of a 64-byte one; FP4
-    // half `sub` is chunk 2*sub + g of a 64-byte row, or chunk g of a 32-byte
-    // one).
+    // half `sub` is chunk 2*sub + g of a 128-byte row, or chunk g of a
+    // 32-byte one).
     auto frag = [&](const uint8_t* base, int r, int sub, auto info, auto rb) __attribute__((always_inline)) -> v8i {
         using I = decltype(info);
         constexpr int RB = decltype(rb)::value;
@@ -428,7 +429,10 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
         else return s7;
     };
     const uint32_t LC0 = lds_addr(c0), LC1 = lds_addr(c1);
-    const int64_t NU = H / SU;  // ring units
+    // ring units; the last one may hold fewer than SU halves (FP4 x FP4 with
+    // K % 256 == 128): its copy also fetches the bytes after the row's end
+    // (the next row's, or zero past the buffer), which no MFMA reads
+    const int64_t NU = (H + SU - 1) / SU;
     // Copies of unit v (clamped to the last unit: a copy past the end lands in
     // a slot that is never read again).
     auto issue_tile = [&](int i, int64_t v, uint32_t dst) __attribute__((always_inline)) {
