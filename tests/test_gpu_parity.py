@@ -101,6 +101,23 @@ def test_per_tensor_ragged_shapes(shape):
     compare_pt(got, exp, f"shape {shape}")
 
 
+@pytest.mark.parametrize("src", ["bf16", "fp32"])
+@pytest.mark.parametrize("delayed", [False, True])
+def test_per_tensor_persistent_tiles(src, delayed):
+    """More tiles than the persistent grid holds blocks (2192 x 7984: 576
+    bf16 tiles of 128 x 256, 1134 fp32 tiles of 128 x 128), ragged in both
+    directions, so blocks walk several tiles, the last ones partial."""
+    g = np.random.Generator(np.random.PCG64([41, int(delayed), src == "bf16"]))
+    shape = (2192, 7984)
+    x = rand_bf16(g, shape, lo_exp=-20, hi_exp=20)
+    if src == "fp32":
+        x = (x.astype(np.uint32) << 16).view(np.float32) * np.float32(1.0 + 2.0 ** -10)
+    hist = np.full(16, 3.0e5, np.float32) if delayed else None
+    got = gpu_quantize_per_tensor(x, 1, history=None if hist is None else hist.copy(), row=True, col=True)
+    exp = O.quantize_per_tensor(x, 1, history=None if hist is None else hist.copy(), row=True, col=True)
+    compare_pt(got, exp, f"persistent {src} delayed={delayed}")
+
+
 def test_delayed_sequence_matches_oracle():
     """Twenty delayed-scaling E5M2 steps on log-normal gradients; the history
     evolves identically (checkpoint/resume: restarting from a copied history
@@ -311,6 +328,19 @@ def test_fp4_col_random(shape, srange):
     oq, os_ = O.fp4_row_to_fp8_col(q4, s4)
     assert np.array_equal(s8, os_)
     assert np.array_equal(q8, oq)
+
+
+def test_fp4_col_persistent_tiles():
+    """4192 x 4192: 561 tiles of 128 x 256 for a persistent grid of 512
+    blocks, ragged in both directions, scales over the whole byte range."""
+    g = np.random.Generator(np.random.PCG64(20))
+    rows, cols = 4192, 4192
+    q4 = g.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    s4 = g.integers(100, 160, size=(rows, cols // 32), dtype=np.uint8)
+    s4[g.integers(0, rows, 64), g.integers(0, cols // 32, 64)] = g.integers(0, 255, 64).astype(np.uint8)
+    q8, s8 = gpu_fp4_col(q4, s4)
+    oq, os_ = O.fp4_row_to_fp8_col(q4, s4)
+    assert np.array_equal(s8, os_) and np.array_equal(q8, oq)
 
 
 def test_fp4_col_specials():
