@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 E4M3, E5M2, E2M1 = 0, 1, 2
-SRC_F32, SRC_BF16 = 0, 1
+SRC_F32, SRC_BF16, SRC_F64 = 0, 1, 2  # float64 input: MX quantizer only
 SCALE_TENSOR, SCALE_BLK32, SCALE_BLK128 = 0, 1, 2
 
 _lib = None
@@ -88,7 +88,9 @@ def _src_of(x):
         return SRC_F32
     if x.dtype == np.uint16:
         return SRC_BF16
-    raise TypeError("oracle input must be float32 or uint16 (bf16 bits)")
+    if x.dtype == np.float64:
+        return SRC_F64
+    raise TypeError("oracle input must be float32, float64 or uint16 (bf16 bits)")
 
 
 # --- O1/O2 ---------------------------------------------------------------
@@ -166,7 +168,8 @@ def quantize_per_tensor(x, fmt, history=None, row=True, col=False):
 # --- O6 --------------------------------------------------------------------
 
 def quantize_mx(x, fmt, row=True, col=False):
-    """Returns (q_row, s_row, q_col, s_col); unrequested outputs are None."""
+    """Returns (q_row, s_row, q_col, s_col); unrequested outputs are None.
+    ``x`` is bf16 bits (uint16), float32 or float64."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
     q_row = s_row = q_col = s_col = None
@@ -181,6 +184,40 @@ def quantize_mx(x, fmt, row=True, col=False):
     lib().or_quantize_mx(_ptr(x), _src_of(x), rows, cols, cols, fmt,
                          _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col))
     return q_row, s_row, q_col, s_col
+
+
+# --- expert MLP activation ----------------------------------------------------
+
+def as_f64(x):
+    """bf16 bits (uint16) or float32 -> float64 (exact)."""
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def silu(x):
+    """SiLU (swish) x * sigma(x) = x / (1 + e^-x), float64 (NaN stays NaN,
+    -inf gives NaN like inf/inf, +inf gives +inf)."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def swiglu(gu, inter):
+    """SwiGLU activation of a gate/up projection output ``gu`` [rows, >= 2
+    inter] (bf16 bits or float32): h = silu(gate) * up, gate in columns
+    [0, inter), up in [inter, 2 inter), float64 [rows, inter]."""
+    v = as_f64(np.ascontiguousarray(gu))
+    with np.errstate(invalid="ignore", over="ignore"):
+        return silu(v[:, :inter]) * v[:, inter:2 * inter]
+
+
+def swiglu_quantize_mx(gu, inter, fmt):
+    """The expert MLP's activation step: h = swiglu(gu) in float64, then MX
+    block-32 quantization along the intermediate dimension (O6 on the
+    float64 values).  Returns (q [rows, inter], s [rows, inter/32], h)."""
+    h = np.ascontiguousarray(swiglu(gu, inter))
+    q, s, _, _ = quantize_mx(h, fmt)
+    return q, s, h
 
 
 # --- O7 --------------------------------------------------------------------

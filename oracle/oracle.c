@@ -36,6 +36,7 @@
 
 #define OR_SRC_F32 0
 #define OR_SRC_BF16 1
+#define OR_SRC_F64 2 /* MX quantizer input only */
 
 #define OR_SCALE_TENSOR 0 /* one float scale_inv for the whole operand */
 #define OR_SCALE_BLK32 1  /* one E8M0 byte per 32 elements along K     */
@@ -238,6 +239,15 @@ static float load_f(const void* x, int src, int64_t i)
     return ((const float*)x)[i];
 }
 
+/* The MX quantizer also takes binary64 input (OR_SRC_F64), for values the
+ * oracle computes in double precision (the SwiGLU activation).            */
+static double load_d(const void* x, int src, int64_t i)
+{
+    if (src == OR_SRC_F64)
+        return ((const double*)x)[i];
+    return (double)load_f(x, src, i);
+}
+
 /* ------------------------------------------------------------------------ */
 /* O3. amax = max |x|.  [FP8 guide], "Transformer Engine: a fundacao de     */
 /* software": the recipe reduces absolute values with "max".  Reading: a NaN */
@@ -413,7 +423,7 @@ void or_quantize_mx(const void* x, int src, int64_t rows, int64_t cols, int64_t 
             unsigned codes[32];
             for (int64_t b = 0; b < cols / 32; ++b) {
                 for (int i = 0; i < 32; ++i)
-                    v[i] = (double)load_f(x, src, r * ld + b * 32 + i);
+                    v[i] = load_d(x, src, r * ld + b * 32 + i);
                 unsigned sb = quantize_block32(fmt, v, codes);
                 s_row[r * (cols / 32) + b] = (uint8_t)sb;
                 for (int i = 0; i < 32; ++i) {
@@ -438,7 +448,7 @@ void or_quantize_mx(const void* x, int src, int64_t rows, int64_t cols, int64_t 
             unsigned codes[32];
             for (int64_t b = 0; b < rows / 32; ++b) {
                 for (int i = 0; i < 32; ++i)
-                    v[i] = (double)load_f(x, src, (b * 32 + i) * ld + c);
+                    v[i] = load_d(x, src, (b * 32 + i) * ld + c);
                 unsigned sb = quantize_block32(fmt, v, codes);
                 s_col[c * (rows / 32) + b] = (uint8_t)sb;
                 for (int i = 0; i < 32; ++i) {
