@@ -177,6 +177,31 @@ int mxq_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, i
                            uint8_t* s8, void* stream);
 
 /*
+ * mxq_swiglu_quantize_mx - the expert MLP's activation between its two
+ * grouped GEMMs: h = silu(gate) * up, then MX block-32 quantization of h
+ * along the intermediate dimension, the A operand of the down-projection.
+ *
+ * Defines: [MoE FP4], "Metodologia" (the expert GEMMs run in FP8, so the
+ * activation between them is requantized to FP8) and "Kernels CUDA
+ * Otimizados" (ragged per-expert rows: the call is row-wise, rows of every
+ * expert alike).  The pages do not name the activation; this library reads
+ * it as SwiGLU, silu(x) = x / (1 + e^-x), with the gate and up projections
+ * side by side in the up-projection's output.
+ *  gu     [rows, ld] elements, src F32 or BF16: gate in columns [0, inter),
+ *         up in [inter, 2 inter)
+ *  q      [rows, inter] FP8 codes (fmt E4M3 or E5M2), dense
+ *  s      [rows, inter/32] E8M0 scale bytes
+ * h is formed in binary32 (exp to within a few ulps, IEEE division), so a
+ * code may differ from one computed on the exact h where h lies within a
+ * few binary32 ulps of a rounding boundary; blocks follow mxq_quantize_mx
+ * (NaN or Inf in h: byte 0xFF, codes 0x7F).
+ * Rules: inter % 32 == 0, ld >= 2 inter; gu and the row pitch 16-byte
+ * aligned; q 8-byte aligned.  The call writes every byte of q and s.
+ */
+int mxq_swiglu_quantize_mx(const void* gu, int src, int64_t rows, int64_t inter, int64_t ld, int fmt, uint8_t* q,
+                           uint8_t* s, void* stream);
+
+/*
  * mxq_scaled_gemm - C = dequant(A) . dequant(B)^T with fp32 accumulation on
  * gfx950's block-scaled MFMA.
  *

@@ -50,6 +50,8 @@ def lib():
         L.mxq_repack_fp4_to_fp8.argtypes = [p, p, p, i64, i64, i64, p, p, p]
         L.mxq_fp4_row_to_fp8_col.restype = i
         L.mxq_fp4_row_to_fp8_col.argtypes = [p, p, i64, i64, p, p, p]
+        L.mxq_swiglu_quantize_mx.restype = i
+        L.mxq_swiglu_quantize_mx.argtypes = [p, i, i64, i64, i64, i, p, p, p]
         L.mxq_scaled_gemm.restype = i
         L.mxq_scaled_gemm.argtypes = [p, i, p, i, p, i, p, i, i64, i64, i64, p, i, i64, p]
         L.mxq_grouped_scaled_gemm.restype = i
@@ -130,6 +132,17 @@ def fp4_row_to_fp8_col(q4, s4, q8, s8, stream=None):
     rows, cols = q4.shape[0], q4.shape[1] * 2
     st = lib().mxq_fp4_row_to_fp8_col(_ptr(q4), _ptr(s4), rows, cols, _ptr(q8), _ptr(s8), _stream(stream))
     _check("mxq_fp4_row_to_fp8_col", st)
+
+
+def swiglu_quantize_mx(gu, inter, fmt, q, s, stream=None):
+    """h = silu(gate) * up of ``gu`` [rows, >= 2 inter] (gate columns [0,
+    inter), up [inter, 2 inter)), MX block-32 quantized into q [rows, inter]
+    and s [rows, inter/32] (mxq_swiglu_quantize_mx)."""
+    rows = gu.shape[0]
+    assert gu.stride(1) == 1
+    st = lib().mxq_swiglu_quantize_mx(_ptr(gu), _src_of(gu), rows, inter, gu.stride(0), fmt, _ptr(q), _ptr(s),
+                                      _stream(stream))
+    _check("mxq_swiglu_quantize_mx", st)
 
 
 def scaled_gemm(A, fa, sA, ma, B, fb, sB, mb, M, N, K, C, out=OUT_F32, ldc=None, stream=None):

@@ -13,6 +13,9 @@ hipError_t launch_quantize_per_tensor(const void* x, int src, int64_t rows, int6
 hipError_t launch_quantize_mx(const void* x, int src, int64_t rows, int64_t cols, int64_t ld, int fmt, uint8_t* q_row,
                               uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t st);
 
+hipError_t launch_swiglu_quantize_mx(const void* gu, int src, int64_t rows, int64_t inter, int64_t ld, int fmt,
+                                     uint8_t* q, uint8_t* s, hipStream_t st);
+
 hipError_t launch_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const int32_t* idx, int64_t src_rows,
                                     int64_t rows, int64_t cols, uint8_t* q8, uint8_t* s8, hipStream_t st);
 hipError_t launch_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, int64_t cols, uint8_t* q8,

@@ -108,6 +108,20 @@ int mxq_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, i
     return hip_status(mxq::launch_fp4_row_to_fp8_col(q4, s4, rows, cols, q8, s8, as_stream(stream)));
 }
 
+int mxq_swiglu_quantize_mx(const void* gu, int src, int64_t rows, int64_t inter, int64_t ld, int fmt, uint8_t* q,
+                           uint8_t* s, void* stream) {
+    if (src != MXQ_SRC_F32 && src != MXQ_SRC_BF16) return MXQ_ERR_FORMAT;
+    if (fmt != MXQ_E4M3 && fmt != MXQ_E5M2) return MXQ_ERR_FORMAT;
+    if (rows < 0 || inter < 0) return MXQ_ERR_SHAPE;
+    if (!gu || !q || !s) return MXQ_ERR_NULL;
+    if (inter % 32 != 0 || ld < 2 * inter) return MXQ_ERR_SHAPE;
+    if (rows * (inter / 8) / 512 + 1 > MAX_GRID_X) return MXQ_ERR_SHAPE;  // 512 vectors per block
+    const int64_t esz = src == MXQ_SRC_BF16 ? 2 : 4;
+    if (!aligned16(gu) || (ld * esz) % 16 != 0 || ((uintptr_t)q & 7u) != 0) return MXQ_ERR_ALIGN;
+    if (rows == 0 || inter == 0) return MXQ_OK;
+    return hip_status(mxq::launch_swiglu_quantize_mx(gu, src, rows, inter, ld, fmt, q, s, as_stream(stream)));
+}
+
 // The GEMM kernel addresses each operand (per group) and its scale array
 // with 32-bit byte offsets.
 static bool below_4gib(int64_t rows, int64_t K, int fmt, int mode) {

@@ -557,6 +557,79 @@ __global__ void __launch_bounds__(256) k_mx_dual(const void* __restrict__ x, int
 }
 
 // ---------------------------------------------------------------------------
+// Expert MLP activation: h = silu(gate) * up of the grouped up-projection's
+// output, MX block-32 quantized along the intermediate dimension for the
+// down-projection GEMM (MoE FP4 page, "Metodologia": the expert GEMMs run
+// in FP8; the activation between them is SwiGLU, silu(x) = x / (1 + e^-x),
+// a reading).  gu [rows, ld] holds the gate in columns [0, inter) and the up
+// projection in [inter, 2 inter).  h is formed in binary32 (expf of -|g|,
+// IEEE division) and quantized like k_mx_row: a lane holds 8 consecutive
+// intermediate columns, an aligned quad of lanes one 32-element block.
+// ---------------------------------------------------------------------------
+constexpr int SWG_VEC_PER_THREAD = 2;
+
+template <int F, int SRC>
+__global__ void __launch_bounds__(256) k_swiglu_mx(const void* __restrict__ gu, int64_t nvec, int64_t vpr,
+                                                   int64_t ld, int64_t inter, uint8_t* __restrict__ q,
+                                                   uint8_t* __restrict__ s) {
+    const int64_t base = (int64_t)blockIdx.x * (256 * SWG_VEC_PER_THREAD) + threadIdx.x;
+    uint32_t gw[SWG_VEC_PER_THREAD][8], uw[SWG_VEC_PER_THREAD][8];
+#pragma unroll
+    for (int it = 0; it < SWG_VEC_PER_THREAD; ++it) {
+        const int64_t v = base + (int64_t)it * 256;
+        const bool ok = v < nvec;
+        const int64_t vc = ok ? v : 0;
+        const int64_t row = vc / vpr, c = (vc - row * vpr) * 8;
+        load8<SRC>(gu, row * ld + c, ok, gw[it]);
+        load8<SRC>(gu, row * ld + inter + c, ok, uw[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < SWG_VEC_PER_THREAD; ++it) {
+        const int64_t v = base + (int64_t)it * 256;
+        if (v >= nvec) continue;  // nvec % 4 == 0: quads stay whole
+        uint32_t h[8];
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            // sigma(g) from e^-|g| in (0, 1], which cannot overflow: very
+            // negative gates keep their (subnormal) products instead of 0
+            const float g = as_float(gw[it][k]);
+            const float en = expf(-__builtin_fabsf(g));
+            const float sg = g >= 0.0f ? 1.0f / (1.0f + en) : en / (1.0f + en);
+            const float y = g * sg * as_float(uw[it][k]);
+            h[k] = as_uint(y);
+            const uint32_t a = h[k] & 0x7FFFFFFFu;
+            m = m > a ? m : a;
+        }
+        m = quad_max_u32(m);  // the 4 lanes of a 32-column block
+        uint32_t lo, hi;
+        uint8_t sb;
+        mx_codes_row8<F>(h, m, lo, hi, sb);
+        st_nt8(q + v * 8, make_uint2(lo, hi));  // rows of q are dense: vector v starts at byte 8 v
+        if ((threadIdx.x & 3) == 0) s[v >> 2] = sb;
+    }
+}
+
+template <int F, int SRC>
+static void launch_swiglu_t(const void* gu, int64_t rows, int64_t inter, int64_t ld, uint8_t* q, uint8_t* s,
+                            hipStream_t st) {
+    const int64_t vpr = inter / 8, nvec = rows * vpr;
+    const unsigned grid = (unsigned)((nvec + 256 * SWG_VEC_PER_THREAD - 1) / (256 * SWG_VEC_PER_THREAD));
+    hipLaunchKernelGGL((k_swiglu_mx<F, SRC>), dim3(grid), dim3(256), 0, st, gu, nvec, vpr, ld, inter, q, s);
+}
+
+hipError_t launch_swiglu_quantize_mx(const void* gu, int src, int64_t rows, int64_t inter, int64_t ld, int fmt,
+                                     uint8_t* q, uint8_t* s, hipStream_t st) {
+    switch (fmt * 2 + src) {
+    case E4M3 * 2 + 0: launch_swiglu_t<E4M3, 0>(gu, rows, inter, ld, q, s, st); break;
+    case E4M3 * 2 + 1: launch_swiglu_t<E4M3, 1>(gu, rows, inter, ld, q, s, st); break;
+    case E5M2 * 2 + 0: launch_swiglu_t<E5M2, 0>(gu, rows, inter, ld, q, s, st); break;
+    case E5M2 * 2 + 1: launch_swiglu_t<E5M2, 1>(gu, rows, inter, ld, q, s, st); break;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <int F, int SRC>

@@ -132,7 +132,8 @@ def tensor(spec, threads=None):
 # 3: E5M2 backward with delayed scaling: dY [4096, 14336] |g| = 2^(3z) random
 #    sign; X [4096, 4096] and W [14336, 4096] as workload 2 without outliers.
 # 4: MXFP4 MoE share: X [8192, 7168] N(0,1); 32 local experts with
-#    W_g [4096 (gate+up), 7168] N(0, 0.02); routing top-8 of 256 uniform.
+#    W_g [4096 (gate+up), 7168] and W_down [7168, 2048] N(0, 0.02); routing
+#    top-8 of 256 uniform.
 # 5: Llama-3-70B MLP, MXFP8: X [8192, 8192], H [8192, 28672] Student-t(3);
 #    W_up [28672, 8192], W_down [8192, 28672] N(0, 0.015); dY [8192, 28672],
 #    dZ [8192, 8192] gradients as workload 3.
@@ -187,6 +188,12 @@ def c4_w(expert):
     """Expert weights [2*2048 (gate and up), 7168]; tensor id 1, one Spec per
     expert keyed by 1000 + expert so every expert has its own stream."""
     return Spec(4, 1000 + expert, 2 * C4_INTER, C4_HIDDEN, "normal", 0.02)
+
+
+def c4_w_down(expert):
+    """Expert down-projection weights [7168 (out), 2048 (in)], N(0, 0.02),
+    stored N x K like every GEMM B operand; keyed by 2000 + expert."""
+    return Spec(4, 2000 + expert, C4_HIDDEN, C4_INTER, "normal", 0.02)
 
 
 def c4_routing():

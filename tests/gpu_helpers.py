@@ -200,3 +200,54 @@ def gemm_scale_arg(s, mode):
     if mode == mxq.SCALE_TENSOR:
         return dev_f32(np.asarray([s], np.float32))
     return dev_u8(s)
+
+
+def check_swiglu_codes(q, s, gu, inter, fmt, what="", rel=2.0 ** -19):
+    """GPU codes/scales of mxq_swiglu_quantize_mx against the oracle, which
+    forms h = silu(gate) * up in float64.  The kernel forms h in binary32 (a
+    few ulps from the exact value, or a few absolute 2^-149 steps where it is
+    subnormal), so where that error can move a decision the GPU may take
+    either side: the block exponent may be any the oracle's rule gives for
+    amax -+ that error, and each code any code between those of
+    (h -+ delta) / 2^e.  Everything else must be identical, and nearly every
+    element bit-identical."""
+    import oracle as O
+    oq, os_, h = O.swiglu_quantize_mx(gu, inter, fmt)
+    rows = h.shape[0]
+    nb = inter // 32
+    hb = h.reshape(rows, nb, 32)
+    bad = ~np.all(np.isfinite(hb), axis=2)
+    qb = q.reshape(rows, nb, 32)
+    assert np.all(s[bad] == 0xFF) and np.all(qb[bad] == 0x7F), f"{what}: NaN blocks"
+    # error bound of the binary32 h: relative rel, plus a few subnormal
+    # steps scaled by |gate * up| (a subnormal sigmoid or product)
+    v = O.as_f64(np.ascontiguousarray(gu))
+    with np.errstate(invalid="ignore", over="ignore"):
+        gmul = np.abs(v[:, :inter] * v[:, inter:2 * inter]).reshape(hb.shape)
+        delta = rel * np.abs(hb) + 2.0 ** -146 * (1.0 + np.nan_to_num(gmul, nan=0.0, posinf=0.0))
+    delta = np.where(bad[:, :, None], 0.0, delta)
+    emax = O.emax(fmt)
+
+    def block_e(a):
+        e = np.full(a.shape, -127, np.int64)
+        pos = a > 0
+        e[pos] = np.floor(np.log2(a[pos])).astype(np.int64) - emax
+        return np.clip(e, -127, 127)
+
+    habs = np.abs(np.where(bad[:, :, None], 0.0, hb))
+    e_lo = block_e(np.maximum(habs - delta, 0).max(axis=2))
+    e_hi = block_e((habs + delta).max(axis=2))
+    eg = s.astype(np.int64) - 127
+    ok_e = bad | ((eg >= e_lo) & (eg <= e_hi))
+    assert ok_e.all(), f"{what}: {int((~ok_e).sum())} block exponents outside the bound"
+    tab = O.decode_table(fmt)
+    scale = np.exp2(-eg.astype(np.float64))[:, :, None]
+    hz = np.where(bad[:, :, None], 0.0, hb)
+    lo = O.cast_array(fmt, np.ascontiguousarray(((hz - delta) * scale).ravel())).reshape(hb.shape)
+    hi = O.cast_array(fmt, np.ascontiguousarray(((hz + delta) * scale).ravel())).reshape(hb.shape)
+    val, vlo, vhi = tab[qb], tab[lo], tab[hi]
+    ok = bad[:, :, None] | ((val >= vlo) & (val <= vhi))
+    assert ok.all(), f"{what}: {int((~ok).sum())} codes outside the bound"
+    same = float(np.mean(q == oq))
+    assert same > 0.999, f"{what}: only {same:.5f} of the codes bit-identical"
+    return same, float(np.mean(s == os_))

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(L, n), n
 
@@ -105,6 +105,21 @@ def test_fp4_col_validation(L):
     assert f(P + 8, P, 64, 64, P, P, None) == EALIGN
     assert f(P, P, 64, 64, P + 8, P, None) == EALIGN
     assert f(P, P, 0, 64, P, P, None) == OK
+
+
+def test_swiglu_validation(L):
+    f = L.mxq_swiglu_quantize_mx
+    assert f(P, 1, 64, 48, 96, 0, P, P, None) == ESHAPE      # inter % 32
+    assert f(P, 1, 64, 64, 100, 0, P, P, None) == ESHAPE     # ld < 2 inter
+    assert f(P, 1, -1, 64, 128, 0, P, P, None) == ESHAPE
+    assert f(P, 1, 64, 64, 128, 2, P, P, None) == EFMT       # FP8 output only
+    assert f(P, 2, 64, 64, 128, 0, P, P, None) == EFMT
+    assert f(None, 1, 64, 64, 128, 0, P, P, None) == ENULL
+    assert f(P, 1, 64, 64, 128, 0, P, None, None) == ENULL
+    assert f(P + 8, 1, 64, 64, 128, 0, P, P, None) == EALIGN
+    assert f(P, 1, 64, 64, 132, 0, P, P, None) == EALIGN     # row pitch of 264 bytes
+    assert f(P, 1, 64, 64, 128, 0, P + 4, P, None) == EALIGN
+    assert f(P, 1, 0, 64, 128, 0, P, P, None) == OK
 
 
 def test_gemm_validation(L):

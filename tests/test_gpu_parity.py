@@ -8,8 +8,9 @@ import torch
 
 import oracle as O
 import mxfp4_precision_numerics_amd as mxq
-from gpu_helpers import (check_gemm, dev_bf16, dev_f32, dev_u8, empty_u8, gemm_scale_arg, gpu_quantize_mx,
-                         gpu_quantize_per_tensor, host, mfma_bound, require_gpu, same_float)
+from gpu_helpers import (check_gemm, check_swiglu_codes, dev_bf16, dev_f32, dev_input, dev_u8, empty_u8,
+                         gemm_scale_arg, gpu_quantize_mx, gpu_quantize_per_tensor, host, mfma_bound, require_gpu,
+                         same_float)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,6 +33,55 @@ def rand_bf16(g, shape, lo_exp=-140, hi_exp=130):
     m = g.integers(0, 128, size=shape, dtype=np.int64)
     s = g.integers(0, 2, size=shape, dtype=np.int64)
     return ((s << 15) | (e << 7) | m).astype(np.uint16)
+
+
+# --------------------------------------------------- expert MLP activation
+
+def gpu_swiglu(gu, inter, fmt, ld=None):
+    rows = gu.shape[0]
+    xd = dev_input(gu)
+    q, sc = empty_u8(rows, inter), empty_u8(rows, inter // 32)
+    mxq.swiglu_quantize_mx(xd, inter, fmt, q, sc)
+    return host(q), host(sc)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("src", ["bf16", "fp32"])
+@pytest.mark.parametrize("shape", [(96, 96), (33, 2080), (256, 512)])
+def test_swiglu_random(fmt, src, shape):
+    """Random gate/up values over a wide exponent range, ragged row counts
+    and block counts; float32 input also with non-bf16 mantissas."""
+    rows, inter = shape
+    g = np.random.Generator(np.random.PCG64([30, fmt, rows, inter, src == "bf16"]))
+    gate = g.standard_normal((rows, inter)) * 4 * np.exp2(g.integers(-6, 4, (rows, 1)))
+    up = g.standard_normal((rows, inter)) * np.exp2(g.integers(-30, 30, (rows, inter // 32)).repeat(32, axis=1))
+    gu = np.concatenate([gate, up], axis=1).astype(np.float32)
+    if src == "bf16":
+        gu = synth_bf16(gu)
+    q, sc = gpu_swiglu(gu, inter, fmt)
+    check_swiglu_codes(q, sc, gu, inter, fmt, f"swiglu {src} fmt{fmt} {shape}")
+
+
+def test_swiglu_specials_and_pitch():
+    """Inf/NaN gates and ups (NaN blocks), gates far out on both sides, zeros
+    with both signs, subnormal products, and a row pitch wider than 2 inter."""
+    rows, inter, ld = 64, 128, 320
+    g = np.random.Generator(np.random.PCG64(31))
+    full = (g.standard_normal((rows, ld)) * 2).astype(np.float32)
+    gate, up = full[:, :inter], full[:, inter:2 * inter]
+    gate[0, 3] = np.inf              # silu(+inf) * up: +-inf -> NaN block
+    gate[1, 40] = -np.inf            # -inf / inf: NaN block
+    up[2, 70] = np.nan
+    gate[3, :32] = -100.0            # silu(-100) * up is a binary32 subnormal
+    gate[4, :32] = 60.0              # sigma = 1
+    gate[5, 32:64] = 0.0             # h = +-0: all-zero block
+    up[5, 64:96] = -0.0
+    gate[6, :] = 1e-30               # products far below binary32's normal range
+    up[6, :] = 1e-15
+    q, sc = gpu_swiglu(full, inter, 0)
+    assert sc[0, 0] == 0xFF and sc[1, 1] == 0xFF and sc[2, 2] == 0xFF
+    assert sc[5, 1] == 0 and np.all(np.isin(q[5, 32:64], (0x00, 0x80)))
+    check_swiglu_codes(q, sc, np.ascontiguousarray(full), inter, 0, "swiglu specials")
 
 
 # ------------------------------------------------------------------ per-tensor
