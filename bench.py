@@ -272,7 +272,28 @@ def measure_rows(torch, mxq, synth, dev, reps):
     r["GB/s"] = round(gbytes / (ms * 1e-3) / 1e9, 1)
     r["frac_hbm"] = round(r["GB/s"] / HBM_PEAK_GBS, 4)
     rows[f"a7 grouped GEMM MXFP8, 32 experts, R={R}, N=4096, K=7168, bf16 out"] = r
-    del q4, s4, q8, s8, qw, sw4, Cg
+    del qw, sw4
+    # the rest of the expert MLP on the up-projection's output: SwiGLU + MX
+    # E4M3, then the down-projection grouped GEMM (N = 7168, K = 2048)
+    qh, sh = torch.empty((R, 2048), **u8), torch.empty((R, 64), **u8)
+    ms = timed(lambda: mxq.swiglu_quantize_mx(Cg, 2048, mxq.E4M3, qh, sh))
+    rows[f"f2 SwiGLU + MX E4M3 of the gate/up output, R={R} x 2048"] = bw(R * (4096 * 2 + 2048 * (1 + 1 / 32)), ms)
+    qd = torch.empty((32, 7168, 2048), **u8)
+    sd = torch.empty((32, 7168, 64), **u8)
+    for e in range(32):
+        wd = bf16(synth.tensor(synth.c4_w_down(e)))
+        mxq.quantize_mx(wd, mxq.E4M3, qd[e], sd[e])
+    del wd
+    Cd = torch.empty((R, 7168), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: mxq.grouped_scaled_gemm(qh, mxq.E4M3, sh, mxq.SCALE_BLK32, qd, mxq.E4M3, sd,
+                                               mxq.SCALE_BLK32, off_d, 32, R, 7168, 2048, Cd, out=mxq.OUT_BF16))
+    gflop = 2.0 * R * 7168 * 2048
+    gbytes = 32 * 7168 * 2048 * (1 + 1 / 32) + R * 2048 * (1 + 1 / 32) + R * 7168 * 2
+    r = fl(gflop, ms, FP8_PEAK_TFLOPS)
+    r["GB/s"] = round(gbytes / (ms * 1e-3) / 1e9, 1)
+    r["frac_hbm"] = round(r["GB/s"] / HBM_PEAK_GBS, 4)
+    rows[f"f2 down-projection grouped GEMM MXFP8, 32 experts, R={R}, N=7168, K=2048, bf16 out"] = r
+    del q4, s4, q8, s8, Cg, qh, sh, qd, sd, Cd
     torch.cuda.empty_cache()
 
     # workload 5: dual MX quantize of H and the 70B up-projection GEMM (MXFP8, and MXFP4 variant)

@@ -196,6 +196,13 @@ def c4_w_down(expert):
     return Spec(4, 2000 + expert, C4_HIDDEN, C4_INTER, "normal", 0.02)
 
 
+def c4_gate_up(rows):
+    """A stand-in for the grouped up-projection's output [rows, 2*2048]
+    (gate | up) with its law: X N(0,1) times W N(0, 0.02) summed over 7168
+    gives N(0, 0.02^2 * 7168), std 1.693.  Tensor id 5."""
+    return Spec(4, 5, rows, 2 * C4_INTER, "normal", 0.02 * float(np.sqrt(C4_HIDDEN)))
+
+
 def c4_routing():
     """Top-8 distinct experts of 256 per token, uniform.  Returns
     (gather_idx int32 [R], group_off int64 [33]): rows sorted by local expert

@@ -15,7 +15,8 @@ import torch
 import oracle as O
 import mxfp4_precision_numerics_amd as mxq
 from mxfp4_precision_numerics_amd import synth
-from gpu_helpers import (check_gemm, dev_bf16, dev_u8, empty_u8, host, mfma_bound, require_gpu)
+from gpu_helpers import (check_gemm, check_swiglu_codes, dev_bf16, dev_u8, empty_u8, host, mfma_bound,
+                         require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -200,6 +201,49 @@ def test_workload4_mxfp4_repack_grouped():
     assert np.all(err <= 2.0 ** -8 * (np.abs(ref) + hb) + hb)
     r = float((np.maximum(err - 2.0 ** -8 * np.abs(ref), 0) / (1e-5 * absum)).max())
     log(f"workload 4 grouped GEMM (bf16 out): max |err - bf16 rounding| / (1e-5 sum) = {r:.3f}")
+
+
+def test_workload4_expert_mlp_activation_and_down_projection():
+    """The rest of the expert MLP: SwiGLU + MX E4M3 quantization of a
+    gate/up output with the up-projection's law (R routed rows x 4096), then
+    the down-projection grouped GEMM (N = 7168, K = 2048) over the 32 local
+    experts on the oracle's codes."""
+    idx, off = synth.c4_routing()
+    R = int(off[-1])
+    gu = synth.tensor(synth.c4_gate_up(R))
+    q = empty_u8(R, 2048)
+    sc = empty_u8(R, 64)
+    mxq.swiglu_quantize_mx(dev_bf16(gu), 2048, 0, q, sc)
+    same, same_s = check_swiglu_codes(host(q), host(sc), gu, 2048, 0, "workload 4 SwiGLU")
+    log(f"workload 4: SwiGLU codes within bound; bit-identical codes {same:.6f}, scales {same_s:.6f}")
+    oq, os_, _ = O.swiglu_quantize_mx(gu, 2048, 0)
+    del gu, q, sc
+    qw = empty_u8(32, 7168, 2048)
+    sw = empty_u8(32, 7168, 64)
+    oqw = np.empty((32, 7168, 2048), np.uint8)
+    osw = np.empty((32, 7168, 64), np.uint8)
+    for e in range(32):
+        w = synth.tensor(synth.c4_w_down(e))
+        mxq.quantize_mx(dev_bf16(w), 0, qw[e], sw[e])
+        oqw[e], osw[e], _, _ = O.quantize_mx(w, 0)
+    assert np.array_equal(host(qw), oqw) and np.array_equal(host(sw), osw)
+    log("workload 4: down-projection weights MXFP8 bit-exact")
+    C = torch.empty((R, 7168), dtype=torch.bfloat16, device="cuda")
+    mxq.grouped_scaled_gemm(dev_u8(oq), 0, dev_u8(os_), 1, qw, 0, sw, 1, torch.from_numpy(off).cuda(), 32, R, 7168,
+                            2048, C, out=mxq.OUT_BF16)
+    g = np.random.Generator(np.random.PCG64(5))
+    m, n = sample_entries(g, R, 7168, 2000)
+    got = (host(C).astype(np.uint32) << 16).view(np.float32)[m, n].astype(np.float64)
+    ref, absum = O.grouped_gemm_entries(oq, 0, os_, 1, oqw, 0, osw, 1, off, 7168, 2048, m, n)
+    grp = np.searchsorted(off, m, side="right") - 1
+    hb = np.empty(len(m))
+    for gi in np.unique(grp):
+        sel = grp == gi
+        hb[sel] = mfma_bound(oq, 0, os_, 1, oqw[gi], 0, osw[gi], 1, 2048, m[sel], n[sel])
+    err = np.abs(got - ref)
+    assert np.all(err <= 2.0 ** -8 * (np.abs(ref) + hb) + hb)
+    r = float((np.maximum(err - 2.0 ** -8 * np.abs(ref), 0) / (1e-5 * absum)).max())
+    log(f"workload 4 down-projection (bf16 out): max |err - bf16 rounding| / (1e-5 sum) = {r:.3f}")
 
 
 @pytest.mark.slow
