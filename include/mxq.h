@@ -191,7 +191,7 @@ int mxq_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, i
  *         up in [inter, 2 inter)
  *  q      [rows, inter] FP8 codes (fmt E4M3 or E5M2), dense
  *  s      [rows, inter/32] E8M0 scale bytes
- * h is formed in binary32 (exp to within a few ulps, IEEE division), so a
+ * h is formed in binary32 (exp and reciprocal each within a few ulps), so a
  * code may differ from one computed on the exact h where h lies within a
  * few binary32 ulps of a rounding boundary; blocks follow mxq_quantize_mx
  * (NaN or Inf in h: byte 0xFF, codes 0x7F).

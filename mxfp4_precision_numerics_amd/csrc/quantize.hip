@@ -562,8 +562,8 @@ __global__ void __launch_bounds__(256) k_mx_dual(const void* __restrict__ x, int
 // down-projection GEMM (MoE FP4 page, "Metodologia": the expert GEMMs run
 // in FP8; the activation between them is SwiGLU, silu(x) = x / (1 + e^-x),
 // a reading).  gu [rows, ld] holds the gate in columns [0, inter) and the up
-// projection in [inter, 2 inter).  h is formed in binary32 (expf of -|g|,
-// IEEE division) and quantized like k_mx_row: a lane holds 8 consecutive
+// projection in [inter, 2 inter).  h is formed in binary32 (expf of -|g|
+// and the hardware reciprocal, a few ulps in all) and quantized like k_mx_row: a lane holds 8 consecutive
 // intermediate columns, an aligned quad of lanes one 32-element block.
 // ---------------------------------------------------------------------------
 constexpr int SWG_VEC_PER_THREAD = 2;
@@ -595,7 +595,7 @@ __global__ void __launch_bounds__(256) k_swiglu_mx(const void* __restrict__ gu, 
             // negative gates keep their (subnormal) products instead of 0
             const float g = as_float(gw[it][k]);
             const float en = expf(-__builtin_fabsf(g));
-            const float sg = g >= 0.0f ? 1.0f / (1.0f + en) : en / (1.0f + en);
+            const float sg = (g >= 0.0f ? 1.0f : en) * __builtin_amdgcn_rcpf(1.0f + en);  // rcp: 1 ulp
             const float y = g * sg * as_float(uw[it][k]);
             h[k] = as_uint(y);
             const uint32_t a = h[k] & 0x7FFFFFFFu;
