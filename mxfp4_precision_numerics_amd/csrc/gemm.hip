@@ -666,7 +666,9 @@ static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     if (rows <= 160 || a.N < 256) return launch_tile<FA, FB, 128, 128>(a, st);
     const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
     if (a.group_off == nullptr && t256 < 192) return launch_tile<FA, FB, 128, 128>(a, st);
-    if (a.group_off != nullptr) return launch_tile<FA, FB, 128, 256>(a, st);
+    // grouped: 256-row tiles once the groups average 192 rows (fewer passes over
+    // each expert's weights), else 128-row tiles
+    if (a.group_off != nullptr && rows < 192) return launch_tile<FA, FB, 128, 256>(a, st);
     return launch_tile<FA, FB, 256, 256>(a, st);
 }
 

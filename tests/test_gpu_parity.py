@@ -556,10 +556,12 @@ def test_gemm_c1_per_tensor_end_to_end():
     check_gemm(C, Cref, Cabs, "c1", hw_bound=hb)
 
 
-def test_grouped_gemm_ragged_with_empty_groups():
-    g = np.random.Generator(np.random.PCG64(700))
-    G, N, K = 6, 256, 512
-    sizes = [0, 37, 256, 0, 129, 1]
+@pytest.mark.parametrize("sizes", [[0, 37, 256, 0, 129, 1], [300, 0, 517, 258]])
+def test_grouped_gemm_ragged_with_empty_groups(sizes):
+    """Ragged groups, empty ones included; the second set averages more than
+    192 rows per group, which selects 256-row tiles (one group spans three)."""
+    g = np.random.Generator(np.random.PCG64([700, len(sizes)]))
+    G, N, K = len(sizes), 256, 512
     off = np.zeros(G + 1, np.int64)
     off[1:] = np.cumsum(sizes)
     R = int(off[-1]) + 13  # trailing rows outside every group stay untouched
