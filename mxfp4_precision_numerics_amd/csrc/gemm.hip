@@ -646,6 +646,20 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
         store_tile(uint16_t{});
 }
 
+// Compute units of the current device (queried once per process).
+static int64_t cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
 template <int FA, int FB, int BM, int BN, bool PRECISE = false>
 static hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
     const int64_t ntn = (a.N + BN - 1) / BN;
@@ -669,6 +683,26 @@ static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     // grouped: 256-row tiles once the groups average 192 rows (fewer passes over
     // each expert's weights), else 128-row tiles
     if (a.group_off != nullptr && rows < 192) return launch_tile<FA, FB, 128, 256>(a, st);
+    if (a.group_off == nullptr) {
+        // A last round of 256 x 256 tiles that would leave half the CUs or
+        // more idle: the columns of whole rounds run as 256 x 256 tiles, the
+        // remaining columns as a second launch of 128 x 256 tiles that fills
+        // one round (each element's sum is the same either way).
+        const int64_t ncu = cu_count(), tm = (a.M + 255) / 256, t = tm * ((a.N + 255) / 256);
+        const int64_t rem = t % ncu, n1 = (t - rem) / tm * 256;
+        if (rem != 0 && rem <= ncu / 2 && n1 > 0 && n1 < a.N &&
+            ((a.M + 127) / 128) * ((a.N - n1 + 255) / 256) <= ncu) {
+            GemmArgs a1 = a, a2 = a;
+            a1.N = n1;
+            a2.N = a.N - n1;
+            a2.B = a.B + n1 * (FB == E2M1 ? a.K / 2 : a.K);
+            if (a.mb != 0) a2.sB = (const uint8_t*)a.sB + n1 * (a.K / (a.mb == 1 ? 32 : 128));
+            a2.C = (uint8_t*)a.C + n1 * (a.out == 0 ? 4 : 2);
+            const hipError_t e = launch_tile<FA, FB, 256, 256>(a1, st);
+            if (e != hipSuccess) return e;
+            return launch_tile<FA, FB, 128, 256>(a2, st);
+        }
+    }
     return launch_tile<FA, FB, 256, 256>(a, st);
 }
 
