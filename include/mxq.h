@@ -196,7 +196,7 @@ int mxq_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, i
  * few binary32 ulps of a rounding boundary; blocks follow mxq_quantize_mx
  * (NaN or Inf in h: byte 0xFF, codes 0x7F).
  * Rules: inter % 32 == 0, ld >= 2 inter; gu and the row pitch 16-byte
- * aligned; q 8-byte aligned.  The call writes every byte of q and s.
+ * aligned; q 16-byte aligned.  The call writes every byte of q and s.
  */
 int mxq_swiglu_quantize_mx(const void* gu, int src, int64_t rows, int64_t inter, int64_t ld, int fmt, uint8_t* q,
                            uint8_t* s, void* stream);

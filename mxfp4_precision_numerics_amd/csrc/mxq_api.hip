@@ -117,7 +117,7 @@ int mxq_swiglu_quantize_mx(const void* gu, int src, int64_t rows, int64_t inter,
     if (inter % 32 != 0 || ld < 2 * inter) return MXQ_ERR_SHAPE;
     if (rows * (inter / 8) / 512 + 1 > MAX_GRID_X) return MXQ_ERR_SHAPE;  // 512 vectors per block
     const int64_t esz = src == MXQ_SRC_BF16 ? 2 : 4;
-    if (!aligned16(gu) || (ld * esz) % 16 != 0 || ((uintptr_t)q & 7u) != 0) return MXQ_ERR_ALIGN;
+    if (!aligned16(gu) || (ld * esz) % 16 != 0 || !aligned16(q)) return MXQ_ERR_ALIGN;
     if (rows == 0 || inter == 0) return MXQ_OK;
     return hip_status(mxq::launch_swiglu_quantize_mx(gu, src, rows, inter, ld, fmt, q, s, as_stream(stream)));
 }

@@ -118,7 +118,7 @@ def test_swiglu_validation(L):
     assert f(P, 1, 64, 64, 128, 0, P, None, None) == ENULL
     assert f(P + 8, 1, 64, 64, 128, 0, P, P, None) == EALIGN
     assert f(P, 1, 64, 64, 132, 0, P, P, None) == EALIGN     # row pitch of 264 bytes
-    assert f(P, 1, 64, 64, 128, 0, P + 4, P, None) == EALIGN
+    assert f(P, 1, 64, 64, 128, 0, P + 8, P, None) == EALIGN
     assert f(P, 1, 0, 64, 128, 0, P, P, None) == OK
 
 
