@@ -273,6 +273,27 @@ def measure_rows(torch, mxq, synth, dev, reps):
     r["frac_hbm"] = round(r["GB/s"] / HBM_PEAK_GBS, 4)
     rows[f"a7 grouped GEMM MXFP8, 32 experts, R={R}, N=4096, K=7168, bf16 out"] = r
     del qw, sw4
+    # variant beyond the pages (which keep the expert GEMMs in FP8): the same
+    # grouped GEMM with MXFP4 weights and MXFP4 activations; the R activation
+    # rows are random E2M1 codes with unit scales (values do not change the
+    # timing)
+    qw4 = torch.empty((32, 4096, 3584), **u8)
+    sw44 = torch.empty((32, 4096, 224), **u8)
+    for e in range(32):
+        we = bf16(synth.tensor(synth.c4_w(e)))
+        mxq.quantize_mx(we, mxq.E2M1, qw4[e], sw44[e])
+    del we
+    Cg4 = torch.empty((R, 4096), dtype=torch.bfloat16, device=dev)
+    qa4 = torch.randint(0, 256, (R, 3584), **u8)
+    sa4 = torch.full((R, 224), 127, **u8)
+    ms = timed(lambda: mxq.grouped_scaled_gemm(qa4, mxq.E2M1, sa4, mxq.SCALE_BLK32, qw4, mxq.E2M1, sw44,
+                                               mxq.SCALE_BLK32, off_d, 32, R, 4096, 7168, Cg4, out=mxq.OUT_BF16))
+    gbytes4 = 32 * 4096 * 7168 * (0.5 + 1 / 32) + R * 7168 * (0.5 + 1 / 32) + R * 4096 * 2
+    r = fl(gflop, ms, FP4_PEAK_TFLOPS)
+    r["GB/s"] = round(gbytes4 / (ms * 1e-3) / 1e9, 1)
+    r["frac_hbm"] = round(r["GB/s"] / HBM_PEAK_GBS, 4)
+    rows[f"a7 variant: grouped GEMM MXFP4 x MXFP4 (no repack), 32 experts, R={R}, N=4096, K=7168, bf16 out"] = r
+    del qw4, sw44, Cg4, qa4, sa4
     # the rest of the expert MLP on the up-projection's output: SwiGLU + MX
     # E4M3, then the down-projection grouped GEMM (N = 7168, K = 2048)
     qh, sh = torch.empty((R, 2048), **u8), torch.empty((R, 64), **u8)

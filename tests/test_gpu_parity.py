@@ -556,6 +556,29 @@ def test_gemm_c1_per_tensor_end_to_end():
     check_gemm(C, Cref, Cabs, "c1", hw_bound=hb)
 
 
+def test_grouped_gemm_fp4_x_fp4():
+    """MXFP4 activations x MXFP4 expert weights (the variant that skips the
+    repack), ragged groups with 256-row tiles: FP4 x FP4 products are exact
+    in the MFMA, so 1e-5 holds."""
+    g = np.random.Generator(np.random.PCG64(701))
+    sizes = [260, 0, 330, 250]  # 210 rows per group on average: 256-row tiles
+    G, N, K = len(sizes), 256, 512
+    off = np.zeros(G + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    R = int(off[-1])
+    A, sA = rand_operand(g, 2, 1, R, K)
+    Bs = [rand_operand(g, 2, 1, N, K) for _ in range(G)]
+    B = np.stack([b for b, _ in Bs])
+    sB = np.stack([s for _, s in Bs])
+    C = torch.empty((R, N), dtype=torch.float32, device="cuda")
+    mxq.grouped_scaled_gemm(dev_u8(A), 2, dev_u8(sA), 1, dev_u8(B), 2, dev_u8(sB), 1,
+                            torch.from_numpy(off).cuda(), G, R, N, K, C)
+    m_idx = np.repeat(np.arange(R), N)
+    n_idx = np.tile(np.arange(N), R)
+    c, cabs = O.grouped_gemm_entries(A, 2, sA, 1, B, 2, sB, 1, off, N, K, m_idx, n_idx)
+    check_gemm(host(C), c.reshape(-1, N), cabs.reshape(-1, N), "grouped fp4")
+
+
 @pytest.mark.parametrize("sizes", [[0, 37, 256, 0, 129, 1], [300, 0, 517, 258]])
 def test_grouped_gemm_ragged_with_empty_groups(sizes):
     """Ragged groups, empty ones included; the second set averages more than
