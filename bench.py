@@ -275,8 +275,8 @@ def measure_rows(torch, mxq, synth, dev, reps):
     del qw, sw4
     # variant beyond the pages (which keep the expert GEMMs in FP8): the same
     # grouped GEMM with MXFP4 weights and MXFP4 activations; the R activation
-    # rows are random E2M1 codes with unit scales (values do not change the
-    # timing)
+    # rows are seeded random E2M1 codes with unit scales (values do not change
+    # the timing)
     qw4 = torch.empty((32, 4096, 3584), **u8)
     sw44 = torch.empty((32, 4096, 224), **u8)
     for e in range(32):
@@ -284,7 +284,9 @@ def measure_rows(torch, mxq, synth, dev, reps):
         mxq.quantize_mx(we, mxq.E2M1, qw4[e], sw44[e])
     del we
     Cg4 = torch.empty((R, 4096), dtype=torch.bfloat16, device=dev)
-    qa4 = torch.randint(0, 256, (R, 3584), **u8)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(41)
+    qa4 = torch.randint(0, 256, (R, 3584), generator=gen, **u8)
     sa4 = torch.full((R, 224), 127, **u8)
     ms = timed(lambda: mxq.grouped_scaled_gemm(qa4, mxq.E2M1, sa4, mxq.SCALE_BLK32, qw4, mxq.E2M1, sw44,
                                                mxq.SCALE_BLK32, off_d, 32, R, 4096, 7168, Cg4, out=mxq.OUT_BF16))
