@@ -124,6 +124,29 @@ def test_per_tensor_every_bf16_pattern(fmt, ref_amax):
         assert np.array_equal(np.nan_to_num(h_gpu), np.nan_to_num(h_or))
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_per_tensor_every_fp32_pattern(fmt):
+    """The saturating RNE cast on every one of the 2^32 binary32 bit patterns
+    (scale pinned to 1 by a history whose max is the format's largest
+    value), in chunks of 2^26 generated on each side from the same counter."""
+    n = 1 << 26
+    rows = n // 4096
+    fmax = np.float32(FMAX[fmt])
+    amax, sc, si = (torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(3))
+    q = empty_u8(rows, 4096)
+    for c in range(1 << 32 >> 26):
+        xd = torch.arange(c * n, (c + 1) * n, dtype=torch.int64, device="cuda").to(torch.int32).view(torch.float32)
+        hist_d = torch.full((16,), float(fmax), dtype=torch.float32, device="cuda")
+        mxq.quantize_per_tensor(xd.view(rows, 4096), fmt, amax, sc, si, q, None, amax_history=hist_d)
+        got = host(q)
+        x = np.arange(c * n, (c + 1) * n, dtype=np.uint64).astype(np.uint32).view(np.float32).reshape(rows, 4096)
+        exp = O.quantize_per_tensor(x, fmt, history=np.full(16, fmax, np.float32), row=True)
+        assert host(sc)[0] == 1.0 and exp["scale"] == 1.0
+        bad = np.nonzero(got != exp["q_row"])
+        assert bad[0].size == 0, (c, bad[0].size, x[bad][:4].view(np.uint32), got[bad][:4], exp["q_row"][bad][:4])
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_per_tensor_random_fp32_bits(fmt):
     g = np.random.Generator(np.random.PCG64(100 + fmt))
