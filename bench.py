@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--row-reps", type=int, default=10)
+    ap.add_argument("--row-reps", type=int, default=10, help="timed repetitions per row (median, p10/p90)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (reference for the traffic counters)")
     return ap.parse_args()
@@ -198,15 +198,20 @@ def measure_rows(torch, mxq, synth, dev, reps):
             b.record(stream)
             b.synchronize()
             ts.append(a.elapsed_time(b))
+        spread[0] = [round(float(np.percentile(ts, q)), 4) for q in (10, 90)]
         return float(np.median(ts))
+
+    spread = [None]  # p10 / p90 of the last timed() call, ms
 
     def bw(nbytes, ms):
         gbs = nbytes / (ms * 1e-3) / 1e9
-        return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        return {"ms": round(ms, 4), "ms_p10_p90": spread[0], "GB/s": round(gbs, 1),
+                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
     def fl(nflop, ms, peak):
         tf = nflop / (ms * 1e-3) / 1e12
-        return {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_peak": round(tf / peak, 4), "peak": peak}
+        return {"ms": round(ms, 4), "ms_p10_p90": spread[0], "TFLOP/s": round(tf, 1), "frac_peak": round(tf / peak, 4),
+                "peak": peak}
 
     rows = {}
     # a1-a3: per-tensor delayed E5M2 cast of dY [4096, 14336] with row + col outputs
