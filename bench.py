@@ -224,6 +224,11 @@ def measure_rows(torch, mxq, synth, dev, reps):
     qr, qc = torch.empty((4096, 14336), **u8), torch.empty((14336, 4096), **u8)
     ms = timed(lambda: mxq.quantize_per_tensor(dy, mxq.E5M2, amax, sc, si, qr, qc, amax_history=hist))
     rows["a1-a3 per-tensor delayed E5M2 cast, dY 4096x14336 bf16, row+col"] = bw(dy.numel() * 4, ms)
+    # current scaling must see the whole tensor's amax before casting: the amax
+    # pass reads dY once more (6 B per element: 2 reads, two 1-byte outputs)
+    amax_c = torch.empty(1, device=dev)
+    ms = timed(lambda: mxq.quantize_per_tensor(dy, mxq.E5M2, amax_c, sc, si, qr, qc))
+    rows["a1-a3 per-tensor current E5M2 (amax pass + cast), dY 4096x14336 bf16, row+col"] = bw(dy.numel() * 6, ms)
     # a6 per-tensor FP8 GEMMs of the backward pass (E5M2 x E4M3)
     w = bf16(synth.tensor(synth.c3_w()))
     qwr, qwc = torch.empty((14336, 4096), **u8), torch.empty((4096, 14336), **u8)
