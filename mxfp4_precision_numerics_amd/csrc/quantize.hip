@@ -1,5 +1,6 @@
-// quantize.hip - amax reduction, per-tensor (current / delayed) scaling and
-// MX block-32 quantization kernels for gfx950.
+// quantize.hip - amax reduction, per-tensor (current / delayed) scaling, MX
+// block-32 quantization and the expert MLP's SwiGLU + MX quantization kernels
+// for gfx950.
 //
 // Per-tensor path: FP8 guide, "Estrategias de escalonamento e estabilidade"
 // (one factor per tensor from its statistics; delayed scaling takes the
