@@ -404,10 +404,11 @@ def test_fp4_col_random(shape, srange):
 
 
 def test_fp4_col_persistent_tiles():
-    """4192 x 4192: 561 tiles of 128 x 256 for a persistent grid of 512
-    blocks, ragged in both directions, scales over the whole byte range."""
+    """5216 x 8224: 1353 tiles of 128 x 256 for a persistent grid of 768
+    blocks (most take two), ragged in both directions, scales over the
+    whole byte range."""
     g = np.random.Generator(np.random.PCG64(20))
-    rows, cols = 4192, 4192
+    rows, cols = 5216, 8224
     q4 = g.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
     s4 = g.integers(100, 160, size=(rows, cols // 32), dtype=np.uint8)
     s4[g.integers(0, rows, 64), g.integers(0, cols // 32, 64)] = g.integers(0, 255, 64).astype(np.uint8)
