@@ -247,7 +247,11 @@ int mxq_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, const uint
  *  group_off  DEVICE int64[G+1], non-decreasing, off[0] = 0,
  *             off[G] <= total_rows.  Empty groups are allowed.  Rows at or
  *             past off[G] are not written.  Offsets are read on the device
- *             only (no host synchronisation).
+ *             only (no host synchronisation), so they cannot be rejected:
+ *             the kernel clamps each to [0, total_rows] (and each group's
+ *             end to at least its start).  Offsets that break the rules
+ *             give unspecified values in C but never an access outside A,
+ *             the scales or C.
  *  C          [total_rows, N] contiguous, fp32 or bf16
  * Rules: as mxq_scaled_gemm (the 4 GiB limit applies to A and to each
  * group's B); G <= 4096.  Rows beyond total_rows are never read, whatever

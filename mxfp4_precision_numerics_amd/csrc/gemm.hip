@@ -100,8 +100,12 @@ __device__ __forceinline__ bool tile_of_block(const GemmArgs& g, Tile& t) {
     const int64_t tn = bid % ntn;
     int64_t mt = bid / ntn;
     for (int64_t gi = 0; gi < g.G; ++gi) {
-        const int64_t r0 = g.group_off[gi], r1 = g.group_off[gi + 1];
-        const int64_t nt = r1 > r0 ? (r1 - r0 + BM - 1) / BM : 0;
+        // offsets clamped to [0, M] (and each end to at least its start):
+        // whatever the device offsets hold, no tile reaches a row outside C
+        const int64_t o0 = g.group_off[gi], o1 = g.group_off[gi + 1];
+        const int64_t r0 = o0 < 0 ? 0 : (o0 > g.M ? g.M : o0);
+        const int64_t r1 = o1 < r0 ? r0 : (o1 > g.M ? g.M : o1);
+        const int64_t nt = (r1 - r0 + BM - 1) / BM;
         if (mt < nt) {
             t.m0 = r0 + mt * BM;
             t.m_end = r1;

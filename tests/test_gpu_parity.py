@@ -629,6 +629,52 @@ def test_grouped_gemm_ragged_with_empty_groups(sizes):
     assert np.all(Ch[int(off[-1]):] == 12345.0)
 
 
+def run_grouped_case(g, off_dev, off_ref, R, N, K):
+    """Grouped MXFP8 GEMM with device offsets `off_dev`; every row of C
+    against the oracle on the offsets `off_ref` (rows outside every group
+    keep their fill value)."""
+    G = len(off_ref) - 1
+    A, sA = rand_operand(g, 0, 2, R, K)
+    B = g.integers(0, 256, size=(G, N, K), dtype=np.uint8)
+    B[(B & 0x7F) == 0x7F] &= 0x3F
+    sB = g.integers(118, 136, size=(G, N, K // 32), dtype=np.uint8)
+    C = torch.full((R, N), 12345.0, dtype=torch.float32, device="cuda")
+    mxq.grouped_scaled_gemm(dev_u8(A), 0, dev_u8(sA), 2, dev_u8(B), 0, dev_u8(sB), 1,
+                            torch.from_numpy(np.asarray(off_dev, np.int64)).cuda(), G, R, N, K, C)
+    Ch = host(C)
+    lo, hi = int(off_ref[0]), int(off_ref[-1])
+    m_idx = np.repeat(np.arange(lo, hi), N)
+    n_idx = np.tile(np.arange(N), hi - lo)
+    c, cabs = O.grouped_gemm_entries(A, 0, sA, 2, B, 0, sB, 1, off_ref, N, K, m_idx, n_idx)
+    hb = np.concatenate([full_bound(A[off_ref[gi]:off_ref[gi + 1]], 0, sA[off_ref[gi]:off_ref[gi + 1]], 2, B[gi], 0,
+                                    sB[gi], 1, int(off_ref[gi + 1] - off_ref[gi]), N, K)
+                         for gi in range(G) if off_ref[gi + 1] > off_ref[gi]])
+    check_gemm(Ch[lo:hi], c.reshape(-1, N), cabs.reshape(-1, N), "grouped", hw_bound=hb)
+    assert np.all(Ch[:lo] == 12345.0) and np.all(Ch[hi:] == 12345.0)
+
+
+def test_grouped_gemm_offsets_clamped_to_the_rows():
+    """Device offsets that break the contract (a negative start, an end past
+    total_rows) cannot be rejected on the host; the kernel clamps them to
+    [0, total_rows], so the result is that of the clamped offsets."""
+    g = np.random.Generator(np.random.PCG64(710))
+    R, N, K = 200, 256, 256
+    run_grouped_case(g, [-5, 40, 40, 100, R + 50], np.array([0, 40, 40, 100, R]), R, N, K)
+
+
+def test_grouped_gemm_most_groups():
+    """G = 4096 (the largest accepted), most groups empty, 1000 rows spread
+    over 60 of them: every block scans the whole offset array."""
+    g = np.random.Generator(np.random.PCG64(711))
+    G, N, K = 4096, 256, 128
+    sizes = np.zeros(G, np.int64)
+    live = np.sort(g.choice(G, 60, replace=False))
+    sizes[live] = g.multinomial(1000 - 60, np.full(60, 1 / 60)) + 1
+    off = np.zeros(G + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    run_grouped_case(g, off, off, int(off[-1]) + 7, N, K)
+
+
 # ---------------------------------------------------- GEMM, precise mode
 
 FP8_PAIRS = [(0, 0), (1, 0), (0, 1), (1, 1)]
