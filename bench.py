@@ -72,8 +72,8 @@ def gemm_traffic():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding of the path is described in DESIGN.md, not run.", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the quantizers and "
+              "GEMMs shard over rows or columns with no communication, which is not run here.", file=sys.stderr)
         sys.exit(2)
     import torch
     import mxfp4_precision_numerics_amd as mxq
