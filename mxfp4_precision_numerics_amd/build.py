@@ -18,7 +18,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxq.so")
-SOURCES = ["mxq_api.hip", "quantize.hip", "repack.hip", "gemm.hip"]
+# (source, object name, extra defines): gemm_inst.hip once per operand-format
+# pair and mode (E4M3 = 0, E5M2 = 1, E2M1 = 2; the precise mode takes FP8
+# operands only), so that the GEMM's instantiations compile in parallel
+SOURCES = [(s, s, []) for s in ("mxq_api.hip", "quantize.hip", "repack.hip", "gemm.hip")]
+SOURCES += [("gemm_inst.hip", f"gemm_inst_{fa}{fb}{p}.hip", [f"-DMXQ_FA={fa}", f"-DMXQ_FB={fb}", f"-DMXQ_PRECISE={p}"])
+            for p in (0, 1) for fa in range(3) for fb in range(3) if p == 0 or (fa < 2 and fb < 2)]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -26,9 +31,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
          "-Wall", "-Wno-unused-function", "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 
-def _compile(src, verbose):
-    out = os.path.join(OBJ, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+def _compile(job, verbose):
+    src, name, defs = job
+    out = os.path.join(OBJ, name + ".o")
+    cmd = [HIPCC, *FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,7 +50,7 @@ def _compile(src, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]

@@ -1,726 +1,30 @@
-// gemm.hip - FP8 / MX block-scaled GEMM (dense and ragged grouped) on
-// gfx950's v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation.
-//
-// MoE FP4 page, "Metodologia": the heavy matrix products stay in FP8 on the
-// matrix units; "Kernels CUDA Otimizados": ragged per-expert token counts.
-// FP8 guide, "MXFP8 e NVFP4": block-scaled FP8 products in hardware.
-//
-// C[m, n] = sum_k deq(A)[m, k] * deq(B)[n, k], A [M, K] and B [N, K] both
-// K-contiguous.  Block scales (E8M0, one byte per 32 or 128 along K) enter
-// the MFMA's per-lane scale operands; a per-tensor factor enters as scale
-// byte 127 (x1) and multiplies the fp32 result in the epilogue.
-//
-// Operand layout of the 32x32x64 scaled MFMA (pinned on the device with
-// one-instruction tests): lane l supplies row l % 32 and the E8M0 scale of
-// K block g = l / 32 (32 elements each).  An FP8 lane holds 32 codes as two
-// 16-byte halves: byte j sits at K = 32 * (j / 16) + 16 * g + j % 16.  An
-// FP4 lane holds K = 32 * g .. +31 in 16 bytes, element 2i in the low nibble
-// of byte i.  Accumulator lane l, register r is row 8 * (r / 4) + 4 * g +
-// r % 4, column l % 32.  The instruction's op_sel picks which byte of the
-// 32-bit scale operand is used.
-//
-// Pipeline.  K runs in halves of 64 elements (one MFMA deep), staged in
-// ring units of whole 128-byte lines per row for operands of one kind (one
-// K step for FP8 x FP8, two for FP4 x FP4) or of one half for mixed
-// FP4 x FP8.  A block (4 waves, 2 x 2 over the tile) keeps a ring of
-// NSL LDS slots of one unit of the A and B tiles each (two for 256 x 256
-// FP8 tiles and for FP4 x FP4, four or eight where they fit), and two slots
-// of scale dwords (a group of four K steps each).  In half j every wave:
-//   * runs the half's MFMAs from fragments already in registers,
-//   * reads the next half's fragments (landed) into the other register set,
-//     interleaved with the MFMAs,
-//   * in the last half of unit u, after a barrier, starts the global->LDS
-//     copies of unit u + NSL into the slot unit u leaves.
-// So copies get NSL - 1 units minus one half to land and LDS reads one
-// half, both hidden behind MFMAs.  The copies are buffer_load ... lds
-// instructions issued from inline assembly: the compiler's wait insertion
-// cannot see them and so adds no conservative waits; the kernel waits for
-// them explicitly (vmcnt) before the barrier that publishes a slot.
-#include <utility>
-
+// gemm.hip - dispatch of the scaled GEMM on its operand formats and mode to
+// the launchers that gemm_inst.hip instantiates (kernels in gemm_kernel.h).
 #include "common.h"
 #include "launch.h"
 
 namespace mxq {
 
-constexpr int NT = 256;  // 4 waves in a 2 x 2 grid, each owning a (BM/2) x (BN/2) sub-tile
-
-template <int F> struct OpInfo {
-    static constexpr int kh = (F == E2M1) ? 32 : 64;  // bytes per row per K half
-    static constexpr int chunks = kh / 16;             // 16-byte chunks per row per half
-    static constexpr int code = FmtInfo<F>::mfma_code;
-};
-
-// LDS byte offset of 16-byte chunk `c` of row `r` in a slot whose rows hold
-// RB bytes (128: eight chunks, 64: four, 32: two).  gfx950's LDS serves a ds_read_b128
-// 16 lanes per clock from 64 four-byte banks (256 bytes), so 16 consecutive
-// lanes (16 consecutive rows of a fragment) must land on 16 distinct 16-byte
-// bank quads; the XOR swizzle on the row bits above those that already
-// spread it gives each of the 16 rows its own quad (measured: 4 clocks per
-// wave-wide read, against 8 without it).
-template <int RB> __device__ __forceinline__ int swz(int r) {
-    static_assert(RB == 128 || RB == 64 || RB == 32, "LDS row bytes");
-    return (RB == 128) ? ((r >> 1) & 7) : (RB == 64) ? ((r >> 2) & 3) : ((r >> 3) & 1);
-}
-template <int RB> __device__ __forceinline__ int lds_off(int r, int c) {
-    return r * RB + ((c ^ swz<RB>(r)) << 4);
-}
-
-struct Tile {
-    int64_t m0, m_end, n0;
-    const uint8_t* B;
-    const uint8_t* sB;
-};
-
-// Map this block to an output tile.  Dense: blocks are dispatched round-robin
-// over the 8 XCDs, so consecutive logical tiles are first gathered onto one
-// XCD (sharing its L2), then ordered GM tile-rows at a time.  Grouped: the
-// m-tiles of all groups, found by scanning the device offsets.
-template <int BM, int BN>
-__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, Tile& t) {
-    const int64_t ntn = (g.N + BN - 1) / BN;
-    int64_t bid = blockIdx.x;
-    t.B = g.B;
-    t.sB = (const uint8_t*)g.sB;
-    if (g.group_off == nullptr) {
-        const int64_t ntm = (g.M + BM - 1) / BM;
-        const int64_t nblk = ntm * ntn;
-        if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
-        constexpr int64_t GM = 4;
-        const int64_t per_group = GM * ntn;
-        const int64_t grp = bid / per_group;
-        const int64_t first = grp * GM;
-        const int64_t gs = (ntm - first) < GM ? (ntm - first) : GM;
-        const int64_t in = bid - grp * per_group;
-        t.m0 = (first + in % gs) * BM;
-        t.m_end = g.M;
-        t.n0 = (in / gs) * BN;
-        return true;
-    }
-    const int64_t tn = bid % ntn;
-    int64_t mt = bid / ntn;
-    for (int64_t gi = 0; gi < g.G; ++gi) {
-        // offsets clamped to [0, M] (and each end to at least its start):
-        // whatever the device offsets hold, no tile reaches a row outside C
-        const int64_t o0 = g.group_off[gi], o1 = g.group_off[gi + 1];
-        const int64_t r0 = o0 < 0 ? 0 : (o0 > g.M ? g.M : o0);
-        const int64_t r1 = o1 < r0 ? r0 : (o1 > g.M ? g.M : o1);
-        const int64_t nt = (r1 - r0 + BM - 1) / BM;
-        if (mt < nt) {
-            t.m0 = r0 + mt * BM;
-            t.m_end = r1;
-            t.n0 = tn * BN;
-            t.B = g.B + gi * g.b_group_stride;
-            t.sB = (const uint8_t*)g.sB + gi * g.sb_group_stride;
-            return true;
-        }
-        mt -= nt;
-    }
-    return false;
-}
-
-// Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>).
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
-// A block-uniform 64-bit value moved to scalar registers.
-__device__ __forceinline__ int64_t uni64(int64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-// Raw buffer resource over `bytes` bytes at `p` (stride 0, gfx9 data format
-// word; loads at or past `bytes` return zero).
-__device__ __forceinline__ v4u make_rsrc(const void* p, int64_t bytes) {
-    const uint64_t a = (uint64_t)p;
-    return v4u{(unsigned)a, (unsigned)(a >> 32) & 0xFFFFu, (unsigned)(uint32_t)bytes, 0x00020000u};
-}
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (LDS and export counters not waited for).
-constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-// 32-bit LDS address of a __shared__ object (what M0 takes below).
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-// Global -> LDS copies: lane L writes bytes [size*L, size*(L+1)) at the
-// wave-uniform LDS address `dst`, from buffer offset voff + soff.
-// The resource, destination and uniform offset are block-uniform; they are
-// passed through readfirstlane so that they sit in scalar registers even
-// where the compiler cannot prove uniformity (free where it can).
-__device__ __forceinline__ v4u uni(const v4u& r) {
-    return v4u{(unsigned)__builtin_amdgcn_readfirstlane(r[0]), (unsigned)__builtin_amdgcn_readfirstlane(r[1]),
-               (unsigned)__builtin_amdgcn_readfirstlane(r[2]), (unsigned)__builtin_amdgcn_readfirstlane(r[3])};
-}
-__device__ __forceinline__ void dma16(const v4u& rsrc, uint32_t voff, uint32_t soff, uint32_t dst) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-                 ::"v"(voff), "s"(uni(rsrc)), "s"(__builtin_amdgcn_readfirstlane(dst)),
-                   "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
-}
-
-
-// One ring unit (RB bytes of K per row) of an operand tile into a slot:
-// each wave copies PER_WAVE 1 KiB pieces (piece i of wave w covers tile rows
-// (w + 4i) * RP ...); lane L's position holds the global chunk that belongs
-// there under the lds_off() swizzle, which is the same for every piece.
-// Rows past the operand's end (a partial last tile) fall outside the
-// buffer's range and read zero; in a grouped operand they read the next
-// group's rows.  Either way they only feed outputs that are never stored.
-// The per-lane offset of piece 0 is kept; piece i adds i * RP * 4 rows, the
-// unit enters as the uniform offset (operands stay below 4 GiB).
-template <int RB, int ROWS>
-struct TileLoader {
-    static constexpr int CH = RB / 16;
-    static constexpr int PER_WAVE = ROWS * RB / 1024 / 4;
-    static constexpr int RP = 1024 / RB;  // rows per 1 KiB piece
-    static_assert(PER_WAVE >= 1 && ROWS * RB % 4096 == 0, "tile unit must split over 4 waves");
-    v4u rsrc;
-    uint32_t off0, step;  // lane offset of piece 0; bytes between pieces
-    __device__ __forceinline__ void init(const uint8_t* base, int64_t bytes, int64_t ld, int64_t row0, int wave,
-                                         int lane) {
-        rsrc = make_rsrc(base, bytes);
-        const int o = wave * 1024 + lane * 16;
-        const int r = o / RB, p = (o % RB) / 16;
-        off0 = (uint32_t)((row0 + r) * ld + ((p ^ swz<RB>(r)) << 4));
-        step = (uint32_t)(4 * RP * ld);
-    }
-    __device__ __forceinline__ void issue(int i, int64_t unit, uint32_t slot, int wave) const {
-        dma16(rsrc, off0 + (uint32_t)i * step, (uint32_t)(unit * RB), slot + (uint32_t)(wave + 4 * i) * 1024u);
-    }
-};
-
-// Scale bytes of a group of SG = 4 K steps, 16 bytes per tile row (one copy
-// per wave).  BLK32: the row's 16 E8M0 bytes of the group's 16 32-blocks
-// (4-aligned since K % 128 == 0).  BLK128: the 16 bytes from the aligned
-// dword that holds the group's first byte, which covers the group's 4 bytes.
-// Per-tensor operands load from offset 0 of their float and never use the
-// data, so that every mode runs the same code.  With 128 rows, waves w and
-// w+2 copy the same rows.  Rows past the end read zero or the next group's
-// scales, as for the tiles.  The buffer range check drops any dword that is
-// not wholly inside the range, so a BLK128 array whose size is not a multiple
-// of 4 gets a range rounded up to the end of its last aligned dword: the last
-// row's bytes arrive, the (unused) padding bytes share that dword's page.
-constexpr int SG = 4;
-template <int ROWS>
-struct ScaleLoader {
-    static_assert(ROWS == 128 || ROWS == 256, "scale rows");
-    v4u rsrc;
-    uint32_t off, kmul, mask;
-    int dst;  // byte offset of this wave's 64 rows within the operand's part of the slot
-    __device__ __forceinline__ void init(int mode, const void* s, int64_t K, int64_t rows, int64_t row0, int wave,
-                                         int lane) {
-        const int64_t pitch = (mode == 1) ? K / 32 : (mode == 2 ? K / 128 : 0);
-        kmul = mode == 1 ? 4u : (mode == 2 ? 1u : 0u);
-        mask = mode == 2 ? ~3u : ~0u;
-        rsrc = make_rsrc(s, mode == 0 ? 4 : (rows * pitch + 3) & ~(int64_t)3);
-        const int r = (wave * 64) % ROWS;
-        dst = r * 16;
-        off = (uint32_t)((row0 + r + lane) * pitch);
-    }
-    __device__ __forceinline__ void issue(int64_t grp, uint32_t slot) const {
-        dma16(rsrc, (off + (uint32_t)(grp * SG) * kmul) & mask, 0u, slot + (uint32_t)dst);
-    }
-};
-
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
-// 2^(b-127) as a float: b = 0 is the subnormal 2^-127, b = 255 NaN.
-__device__ __forceinline__ float e8m0_f32(uint32_t b) {
-    uint32_t bits = b << 23;
-    bits = b == 0 ? 0x00400000u : bits;
-    bits = b == 255 ? 0x7FC00000u : bits;
-    return __builtin_bit_cast(float, bits);
-}
-
-// Bytes 8q .. 8q+7 of an FP8 fragment (dwords 2q, 2q+1) as 8 bf16 values
-// times `scale`.  The packed results are taken whole as 32-bit words.
-template <int F> __device__ __forceinline__ v8bf to_bf16(const v8i& f, int q, float scale) {
-    const uint32_t d0 = (uint32_t)f[2 * q], d1 = (uint32_t)f[2 * q + 1];
-    uint32_t w[4];
-    if constexpr (F == E4M3) {
-        w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false));
-        w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true));
-        w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false));
-        w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true));
-    } else {
-        w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d0, scale, false));
-        w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d0, scale, true));
-        w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, scale, false));
-        w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, scale, true));
-    }
-    const uint4 u{w[0], w[1], w[2], w[3]};
-    return __builtin_bit_cast(v8bf, u);
-}
-
-// Copy instructions a wave issues at the last half (position J mod 8) of a
-// ring unit: TL tile copies, plus the 2 scale-group copies at position JS.
-constexpr int copies_at(int J, int TL, int JS) { return TL + ((J % 8 + 8) % 8 == JS ? 2 : 0); }
-// Copies issued at the last halves of the NSL-2 units before the unit that
-// ends at position J (still allowed in flight when that half waits for the
-// next unit's copies); units are SU halves long.
-constexpr int copies_after(int J, int NSL, int SU, int TL, int JS) {
-    int n = 0;
-    for (int d = 1; d <= NSL - 2; ++d) n += copies_at(J - d * SU, TL, JS);
-    return n;
-}
-
-// PRECISE: both operands FP8; each FP8 fragment is converted in registers to
-// bf16 with its E8M0 scale folded in (exact: the converter rounds value x
-// 2^e to bf16, which holds every FP8 value times any power of two inside
-// bf16's range), then v_mfma_f32_32x32x16_bf16 accumulates the exact
-// products in fp32.  Slower than the block-scaled FP8 MFMA, whose products
-// are truncated to 13 fractional bits inside each run of 8 K positions.
-template <int FA, int FB, int BM, int BN, bool PRECISE = false>
-__global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
-    static_assert(!PRECISE || (FA != E2M1 && FB != E2M1), "precise mode takes FP8 operands");
-    using IA = OpInfo<FA>;
-    using IB = OpInfo<FB>;
-    // Ring unit: SU K halves.  Copies fetch RB contiguous bytes per row, and
-    // partial-line copies cost the CU's address unit about as much as whole
-    // ones, so operands of one kind stage whole 128-byte lines per row and
-    // unit: one K step for FP8 x FP8, two for FP4 x FP4.  Mixed FP4 x FP8
-    // stages one K half.
-    constexpr bool SAME = (FA == E2M1) == (FB == E2M1);
-    constexpr int SU = SAME ? (FA == E2M1 ? 4 : 2) : 1;
-    constexpr int RBA = SU * IA::kh, RBB = SU * IB::kh;  // bytes per row per unit
-    constexpr int A_H = BM * RBA, B_H = BN * RBB;        // bytes of one unit of each tile
-    constexpr int SLOT = A_H + B_H;
-    constexpr int SCB = 16 * (BM + BN);                    // scale bytes of a group of SG K steps
-    constexpr int FM = BM / 64, FN = BN / 64;              // 32-row fragments per wave
-    constexpr int WN = BN / 2;                             // columns of a wave's sub-tile
-    constexpr int NM = FM * FN;                            // MFMAs per half
-    // ring slots: eight, four or two, the most that fit in LDS (a power of
-    // two that divides the 8 / SU units of the unrolled group of eight halves)
-    constexpr int LDS_BYTES = 160 * 1024;
-    constexpr int NSL = (SU == 1 && 8 * SLOT + 2 * SCB <= LDS_BYTES) ? 8
-                        : (SU <= 2 && 4 * SLOT + 2 * SCB <= LDS_BYTES ? 4 : 2);
-    static_assert(NSL * SLOT + 2 * SCB <= LDS_BYTES, "ring must fit in LDS");
-    constexpr int SLOT_MID = NSL >= 4 ? SLOT : 16;
-    constexpr int SLOT_HI = NSL == 8 ? SLOT : 16;
-    // separate arrays, so the slots are distinct objects to the compiler
-    __shared__ __attribute__((aligned(16))) uint8_t s0[SLOT], s1[SLOT], s2[SLOT_MID], s3[SLOT_MID];
-    __shared__ __attribute__((aligned(16))) uint8_t s4[SLOT_HI], s5[SLOT_HI], s6[SLOT_HI], s7[SLOT_HI];
-    __shared__ __attribute__((aligned(16))) uint8_t c0[SCB], c1[SCB];
-
-    Tile t;
-    if (!tile_of_block<BM, BN>(g, t)) return;
-    // the tile is the same for the whole block: keep it in scalar registers
-    t.m0 = uni64(t.m0);
-    t.m_end = uni64(t.m_end);
-    t.n0 = uni64(t.n0);
-    t.B = (const uint8_t*)uni64((int64_t)t.B);
-    t.sB = (const uint8_t*)uni64((int64_t)t.sB);
-    const int tid = threadIdx.x, lane = tid & 63;
-    // wave index in a scalar register: LDS copy destinations stay scalar
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t lda = (FA == E2M1) ? g.K / 2 : g.K;  // bytes per row
-    const int64_t ldb = (FB == E2M1) ? g.K / 2 : g.K;
-    const int64_t nks = g.K / 128, H = 2 * nks;         // K steps, K halves
-    const int gq = lane >> 5;                            // K block of the instruction this lane feeds
-    const int64_t pA = g.ma == 1 ? g.K / 32 : g.K / 128;  // scale pitch of the operand rows
-    const int64_t pB = g.mb == 1 ? g.K / 32 : g.K / 128;
-    const int rA = wm * (BM / 2) + (lane & 31), rB = wn * (BN / 2) + (lane & 31);
-
-    // operand extents for the buffer resources (validated below 4 GiB); a
-    // grouped A has M = total rows, whatever its offsets claim
-    TileLoader<RBA, BM> ldA;
-    TileLoader<RBB, BN> ldB;
-    ldA.init(g.A, g.M * lda, lda, t.m0, wave, lane);
-    ldB.init(t.B, g.N * ldb, ldb, t.n0, wave, lane);
-    ScaleLoader<BM> lsA;
-    ScaleLoader<BN> lsB;
-    lsA.init(g.ma, g.sA, g.K, g.M, t.m0, wave, lane);
-    lsB.init(g.mb, t.sB, g.K, g.N, t.n0, wave, lane);
-    constexpr int TLA = TileLoader<RBA, BM>::PER_WAVE;
-    constexpr int TL = TLA + TileLoader<RBB, BN>::PER_WAVE;  // tile copies per unit
-
-    // Scale operand of a fragment row, from the staged dword: the byte for K
-    // half h ends up at byte 2h (BLK32: blocks 2h + gq; BLK128: the step's
-    // byte copied to bytes 0 and 2); per-tensor: 127 (x1) everywhere.  The
-    // mode is folded into a shift, two masks and an OR value chosen once
-    // (full-rate shifts and logic only):
-    //   b = (d >> ((sh + 8 ks k) & 31)) & mask;  s = b | ((b << 16) & dup) | orv
-    struct SMode { uint32_t k, mask, dup, orv; };
-    auto smode = [](int mode) __attribute__((always_inline)) -> SMode {
-        if (mode == 0) return {0u, 0u, 0u, 0x7F7F7F7Fu};
-        if (mode == 1) return {0u, ~0u, 0u, 0u};
-        return {1u, 0xFFu, 0xFFFF0000u, 0u};
-    };
-    const SMode smA = smode(g.ma), smB = smode(g.mb);
-    // (row * pitch) % 4 is the same for every fragment row of this lane: rows
-    // differ by multiples of 32
-    const uint32_t rdA = (uint32_t)(((t.m0 + rA) * pA) & 3), rdB = (uint32_t)(((t.n0 + rB) * pB) & 3);
-    const uint32_t shA = g.ma == 1 ? 8u * gq : 8u * rdA;
-    const uint32_t shB = g.mb == 1 ? 8u * gq : 8u * rdB;
-    // byte offset, within a row's 16 staged bytes, of the dword holding step
-    // ks's scale(s): BLK32 dword ks % 4; BLK128 the dword of byte rd + ks % 4
-    const uint32_t kmA = g.ma == 1 ? 4u : 1u, kmB = g.mb == 1 ? 4u : 1u;
-    const uint32_t rdA_ = g.ma == 2 ? rdA : 0u, rdB_ = g.mb == 2 ? rdB : 0u;
-    auto dwA = [&](int64_t ks) __attribute__((always_inline)) -> uint32_t { return ((((uint32_t)ks & 3u) * kmA + rdA_) >> 2) * 4u; };
-    auto dwB = [&](int64_t ks) __attribute__((always_inline)) -> uint32_t { return ((((uint32_t)ks & 3u) * kmB + rdB_) >> 2) * 4u; };
-
-    // register sets: fragments of two halves, scale operands of two K steps
-    v8i fa[2][FM], fb[2][FN];
-    uint32_t sa[2][FM], sb[2][FN];
-    v16f acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
-
-    // Fragment of rows r .. r+31 for K half `sub` of a unit (chunk indexes
-    // within an RB-byte row: FP8 half `sub` is chunks 4*sub + g and
-    // 4*sub + 2 + g of a 128-byte row, or g and 2+g of a 64-byte one; FP4
-    // half `sub` is chunk 2*sub + g of a 128-byte row, or chunk g of a
-    // 32-byte one).
-    auto frag = [&](const uint8_t* base, int r, int sub, auto info, auto rb) __attribute__((always_inline)) -> v8i {
-        using I = decltype(info);
-        constexpr int RB = decltype(rb)::value;
-        if constexpr (I::kh == 32) {
-            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, 2 * sub + gq));
-            return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        } else {
-            constexpr int C0 = RB == 128 ? 4 : 0;  // first chunk of half `sub`: C0 * sub
-            const uint4 x = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, C0 * sub + gq));
-            const uint4 y = *reinterpret_cast<const uint4*>(base + lds_off<RB>(r, C0 * sub + 2 + gq));
-            return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-        }
-    };
-    auto frag_a = [&](const uint8_t* slot, int i, int sub) __attribute__((always_inline)) -> v8i {
-        return frag(slot, rA + 32 * i, sub, IA{}, std::integral_constant<int, RBA>{});
-    };
-    auto frag_b = [&](const uint8_t* slot, int j, int sub) __attribute__((always_inline)) -> v8i {
-        return frag(slot + A_H, rB + 32 * j, sub, IB{}, std::integral_constant<int, RBB>{});
-    };
-    // shift of step ks for an operand (the same for all its fragment rows)
-    auto sshift = [&](const SMode& m, uint32_t sh, int64_t ks) __attribute__((always_inline)) -> uint32_t {
-        return (sh + 8u * ((uint32_t)ks & 3u) * m.k) & 31u;
-    };
-    auto sreg = [&](const SMode& m, uint32_t d, uint32_t shift) __attribute__((always_inline)) -> uint32_t {
-        if constexpr (PRECISE) {
-            // byte 2h + b holds the scale of K block b of half h: BLK32 the
-            // staged dword itself, BLK128 its step byte in all four bytes
-            if (m.orv) return m.orv;
-            if (m.dup == 0) return d;
-            return ((d >> shift) & 0xFFu) * 0x01010101u;
-        } else {
-            const uint32_t b = (d >> shift) & m.mask;
-            return b | ((b << 16) & m.dup) | m.orv;
-        }
-    };
-
-    // slot I of the ring (compile-time I)
-    auto slot = [&](auto I_) __attribute__((always_inline)) -> uint8_t* {
-        constexpr int I = decltype(I_)::value;
-        if constexpr (I == 0) return s0;
-        else if constexpr (I == 1) return s1;
-        else if constexpr (I == 2) return s2;
-        else if constexpr (I == 3) return s3;
-        else if constexpr (I == 4) return s4;
-        else if constexpr (I == 5) return s5;
-        else if constexpr (I == 6) return s6;
-        else return s7;
-    };
-    const uint32_t LC0 = lds_addr(c0), LC1 = lds_addr(c1);
-    // ring units; the last one may hold fewer than SU halves (FP4 x FP4 with
-    // K % 256 == 128): its copy also fetches the bytes after the row's end
-    // (the next row's, or zero past the buffer), which no MFMA reads
-    const int64_t NU = (H + SU - 1) / SU;
-    // Copies of unit v (clamped to the last unit: a copy past the end lands in
-    // a slot that is never read again).
-    auto issue_tile = [&](int i, int64_t v, uint32_t dst) __attribute__((always_inline)) {
-        const int64_t vc = v < NU ? v : NU - 1;
-        if (i < TLA)
-            ldA.issue(i, vc, dst, wave);
-        else
-            ldB.issue(i - TLA, vc, dst + (uint32_t)A_H, wave);
-    };
-    // Scale group u (K steps 4u .. 4u+3) into scale slot u % 2.
-    auto issue_scales = [&](int64_t grp) __attribute__((always_inline)) {
-        const uint32_t cs = LC0 + (uint32_t)(grp & 1) * (LC1 - LC0);  // (a select here defeats SROA)
-        lsA.issue(grp, cs);
-        lsB.issue(grp, cs + 16u * BM);
-    };
-    // Schedule: unit v (halves SU*v ..) lives in slot v % NSL.  Its copies are
-    // issued in the last half of unit v - NSL, right after that half's
-    // barrier (all reads of the slot are done by then); the prologue issues
-    // units 0 .. NSL-1.  The scale group that starts at half 8u is issued
-    // first, with the copies of the unit holding half 8u; its issuing half
-    // sits at position JS (mod 8):
-    constexpr int JS = ((8 - NSL * SU + SU - 1) % 8 + 8) % 8;
-    static_assert(NSL * TL + 2 <= 63, "copies in flight must fit the vmcnt counter");
-    static_assert((8 / SU) % NSL == 0, "slots must repeat within a group of eight halves");
-
-    // One half j at position J = j % 8 of a group of eight halves (four K
-    // steps): MFMAs of half j from register set j % 2 while the fragments of
-    // half j+1 are read into the other set.  In the last half of a unit the
-    // half waits for the next unit's copies, passes a barrier and refills
-    // the unit's slot with unit + NSL.  At odd positions half j+1 starts a K
-    // step: its scales are read and its scale operands formed.
-    auto half = [&](int64_t j, auto J_) __attribute__((always_inline)) {
-        constexpr int J = decltype(J_)::value;
-        constexpr int P = J & 1, Q = 1 - P;       // register set of half j, of half j+1
-        constexpr int SP = (J >> 1) & 1;          // scale set of half j's K step
-        constexpr bool RS = (J & 1) == 1;         // read the scales of step (j+1)/2
-        constexpr int SQ = ((J + 1) >> 1) & 1;    // their scale set
-        constexpr int SUB = J % SU, SUB1 = (J + 1) % SU;       // halves within units
-        constexpr bool LAST = SUB == SU - 1;      // last half of its unit
-        constexpr int CUR = (J / SU) % NSL, NXT = ((J + 1) / SU) % NSL;
-        uint32_t dst = 0;
-        if constexpr (LAST) {
-            // wait for the next unit's copies; those of the NSL-2 units
-            // issued after them may still run
-            __builtin_amdgcn_s_waitcnt(wait_vm(copies_after(J, NSL, SU, TL, JS)));
-            __syncthreads();
-            __builtin_amdgcn_sched_barrier(0);
-            dst = lds_addr(slot(std::integral_constant<int, CUR>{}));
-            if constexpr (J == JS) issue_scales((j + 1 + (NSL - 1) * SU) / (2 * SG));
-        }
-        uint32_t da[FM], db[FN];
-        if constexpr (RS) {
-            const int64_t ks = (j + 1) / 2;
-            const uint8_t* cs = ((ks / SG) & 1) ? c1 : c0;
-            const uint32_t oa = dwA(ks), ob = dwB(ks);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) da[i] = *reinterpret_cast<const uint32_t*>(cs + (rA + 32 * i) * 16 + oa);
-#pragma unroll
-            for (int jj = 0; jj < FN; ++jj)
-                db[jj] = *reinterpret_cast<const uint32_t*>(cs + 16 * BM + (rB + 32 * jj) * 16 + ob);
-        }
-        const uint8_t* nxt = slot(std::integral_constant<int, NXT>{});
-        static_for<NM>([&](auto kc) __attribute__((always_inline)) {
-            constexpr int k = decltype(kc)::value;
-            constexpr int i = k % FM, jj = k / FM;
-            if constexpr (!PRECISE) {
-                acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    fa[P][i], fb[P][jj], acc[i][jj], IA::code, IB::code, 2 * P, (int)sa[SP][i], 2 * P,
-                    (int)sb[SP][jj]);
-            } else {
-                // four bf16 instructions of K = 16, one per quarter q of the
-                // fragment bytes (the same bytes of A and B, so the same K);
-                // quarter q lies in K block q / 2 of this half
-                static_for<4>([&](auto qc) __attribute__((always_inline)) {
-                    constexpr int q = decltype(qc)::value;
-                    constexpr int sh = 8 * (2 * P + q / 2);
-                    const v8bf a8 = to_bf16<FA>(fa[P][i], q, e8m0_f32((sa[SP][i] >> sh) & 0xFFu));
-                    const v8bf b8 = to_bf16<FB>(fb[P][jj], q, e8m0_f32((sb[SP][jj] >> sh) & 0xFFu));
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, acc[i][jj], 0, 0, 0);
-                });
-            }
-            // next half's fragments, one per MFMA while they last
-            if constexpr (k < FM) fa[Q][k] = frag_a(nxt, k, SUB1);
-            if constexpr (k >= FM && k < FM + FN) fb[Q][k - FM] = frag_b(nxt, k - FM, SUB1);
-            // copies of unit + NSL, spread evenly over the half's MFMAs (a copy
-            // waits for the CU's address unit; bursts stall the MFMAs)
-            if constexpr (LAST) {
-                static_for<TL>([&](auto ic) __attribute__((always_inline)) {
-                    constexpr int c = decltype(ic)::value;
-                    if constexpr (TL <= NM) {
-                        if constexpr (k == (2 * c + 1) * NM / (2 * TL)) issue_tile(c, j / SU + NSL, dst);
-                    } else {
-                        if constexpr (k == c * NM / TL) issue_tile(c, j / SU + NSL, dst);
-                    }
-                });
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        if constexpr (RS) {
-            const int64_t ks = (j + 1) / 2;
-            const uint32_t xa = sshift(smA, shA, ks), xb = sshift(smB, shB, ks);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) sa[SQ][i] = sreg(smA, da[i], xa);
-#pragma unroll
-            for (int jj = 0; jj < FN; ++jj) sb[SQ][jj] = sreg(smB, db[jj], xb);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // prologue: scale group 0 and units 0 .. NSL-1 in flight; half 0 and
-    // step 0's scales read
-    issue_scales(0);
-    static_for<NSL>([&](auto uc) __attribute__((always_inline)) {
-        const uint32_t dst = lds_addr(slot(uc));
-        static_for<TL>([&](auto ic) __attribute__((always_inline)) {
-            issue_tile(decltype(ic)::value, decltype(uc)::value, dst);
-        });
-    });
-    __builtin_amdgcn_s_waitcnt(wait_vm((NSL - 1) * TL));
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        fa[0][i] = frag_a(s0, i, 0);
-        sa[0][i] = sreg(smA, *reinterpret_cast<const uint32_t*>(c0 + (rA + 32 * i) * 16 + dwA(0)), sshift(smA, shA, 0));
-    }
-#pragma unroll
-    for (int jj = 0; jj < FN; ++jj) {
-        fb[0][jj] = frag_b(s0, jj, 0);
-        sb[0][jj] = sreg(smB, *reinterpret_cast<const uint32_t*>(c0 + 16 * BM + (rB + 32 * jj) * 16 + dwB(0)), sshift(smB, shB, 0));
-    }
-
-    // groups of eight halves; then the 0, 2, 4 or 6 that remain
-    int64_t j = 0;
-    for (; j + 8 <= H; j += 8)
-        static_for<8>([&](auto Jc) __attribute__((always_inline)) { half(j + decltype(Jc)::value, Jc); });
-    static_for<7>([&](auto Jc) __attribute__((always_inline)) {
-        if (j + decltype(Jc)::value < H) half(j + decltype(Jc)::value, Jc);
-    });
-    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // every copy has landed before the slots are reused
-    __syncthreads();
-
-    // Epilogue: per-tensor factors, then fp32 or bf16 (round to nearest even).
-    // Each wave stages bands of BR rows of its sub-tile in one slot (free
-    // once the last barrier has passed) and writes them back as whole rows
-    // of 16-byte stores.
-    float alpha = 1.0f;
-    if (g.ma == 0) alpha *= ((const float*)g.sA)[0];
-    if (g.mb == 0) alpha *= ((const float*)g.sB)[0];
-    const int64_t row_base = t.m0 + wm * (BM / 2), col_base = t.n0 + wn * WN;
-    // rows and columns of this wave's sub-tile that exist in C
-    const int mlim = (int)min(t.m_end - row_base, (int64_t)(BM / 2));
-    const int nlim = (int)min(g.N - col_base, (int64_t)WN);
-    // staging room per wave: a slot each, or half of slot 0 / 1 with two slots
-    constexpr int CAP = NSL >= 4 ? SLOT : SLOT / 2;
-    uint8_t* const mine = NSL >= 4 ? (wave == 0 ? s0 : wave == 1 ? s1 : wave == 2 ? s2 : s3)
-                                   : (wave < 2 ? s0 : s1) + (wave & 1) * CAP;
-    auto store_tile = [&](auto tag) __attribute__((always_inline)) {
-        using T = decltype(tag);
-        constexpr int PER = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-        constexpr int CPR = WN / PER;             // chunks per row
-        constexpr int RPI = 64 / CPR;             // rows per wave-wide read
-        constexpr int BR = (32 * WN * (int)sizeof(T) <= CAP) ? 32 : (16 * WN * (int)sizeof(T) <= CAP ? 16 : 8);
-        static_assert(BR * WN * (int)sizeof(T) <= CAP && BR % RPI == 0, "epilogue band");
-        constexpr int RB = BR / 2;                // accumulator registers per band (8 rows <-> 4 registers)
-        T* band = reinterpret_cast<T*>(mine);
-        T* cw = (T*)g.C + row_base * g.ldc + col_base;
-        const int cc = (lane % CPR) * PER;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int b = 0; b < 32 / BR; ++b) {
-#pragma unroll
-                for (int jj = 0; jj < FN; ++jj)
-#pragma unroll
-                    for (int r = RB * b; r < RB * (b + 1); ++r) {
-                        const float v = acc[i][jj][r] * alpha;
-                        T o;
-                        if constexpr (sizeof(T) == 4) {
-                            o = v;
-                        } else {
-                            const uint32_t u = as_uint(v);
-                            const uint32_t rn = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-                            o = (T)(((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : rn);
-                        }
-                        band[(8 * (r / 4) + 4 * gq + (r % 4) - BR * b) * WN + 32 * jj + (lane & 31)] = o;
-                    }
-                __syncthreads();
-#pragma unroll
-                for (int q = 0; q < BR / RPI; ++q) {
-                    const int br = q * RPI + lane / CPR;
-                    const int rr = 32 * i + BR * b + br;
-                    const uint4 d = *reinterpret_cast<const uint4*>(band + br * WN + cc);
-                    if (rr < mlim) {
-                        T* dst = cw + (int64_t)rr * g.ldc + cc;
-                        if (cc + PER <= nlim) {
-                            *reinterpret_cast<uint4*>(dst) = d;
-                        } else {
-                            const T* e = reinterpret_cast<const T*>(&d);
-#pragma unroll
-                            for (int k = 0; k < PER; ++k)
-                                if (cc + k < nlim) dst[k] = e[k];
-                        }
-                    }
-                }
-                __syncthreads();
-            }
-    };
-    if (g.out == 0)
-        store_tile(float{});
-    else
-        store_tile(uint16_t{});
-}
-
-// Compute units of the current device (queried once per process).
-static int64_t cu_count() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
-}
-
-template <int FA, int FB, int BM, int BN, bool PRECISE = false>
-static hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
-    const int64_t ntn = (a.N + BN - 1) / BN;
-    const int64_t ntm = (a.group_off == nullptr) ? (a.M + BM - 1) / BM : (a.M + BM - 1) / BM + a.G;
-    hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE>), dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a);
-    return hipGetLastError();
-}
-
-// Tile choice: the largest tiles (most operand reuse per LDS byte) unless
-// they leave most of the 256 CUs idle.  The precise mode uses 128 x 128
-// tiles (room for the converted operands).
-template <int FA, int FB>
-static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
-    if constexpr (FA != E2M1 && FB != E2M1) {
-        if (a.precise) return launch_tile<FA, FB, 128, 128, true>(a, st);
-    }
-    const int64_t rows = a.group_off ? (a.M / (a.G > 0 ? a.G : 1)) : a.M;
-    if (rows <= 160 || a.N < 256) return launch_tile<FA, FB, 128, 128>(a, st);
-    const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (a.group_off == nullptr && t256 < 192) return launch_tile<FA, FB, 128, 128>(a, st);
-    // grouped: 256-row tiles once the groups average 192 rows (fewer passes over
-    // each expert's weights), else 128-row tiles
-    if (a.group_off != nullptr && rows < 192) return launch_tile<FA, FB, 128, 256>(a, st);
-    if (a.group_off == nullptr) {
-        // A last round of 256 x 256 tiles that would leave half the CUs or
-        // more idle: the columns of whole rounds run as 256 x 256 tiles, the
-        // remaining columns as a second launch of 128 x 256 tiles that fills
-        // one round (each element's sum is the same either way).
-        const int64_t ncu = cu_count(), tm = (a.M + 255) / 256, t = tm * ((a.N + 255) / 256);
-        const int64_t rem = t % ncu, n1 = (t - rem) / tm * 256;
-        if (rem != 0 && rem <= ncu / 2 && n1 > 0 && n1 < a.N &&
-            ((a.M + 127) / 128) * ((a.N - n1 + 255) / 256) <= ncu) {
-            GemmArgs a1 = a, a2 = a;
-            a1.N = n1;
-            a2.N = a.N - n1;
-            a2.B = a.B + n1 * (FB == E2M1 ? a.K / 2 : a.K);
-            if (a.mb != 0) a2.sB = (const uint8_t*)a.sB + n1 * (a.K / (a.mb == 1 ? 32 : 128));
-            a2.C = (uint8_t*)a.C + n1 * (a.out == 0 ? 4 : 2);
-            const hipError_t e = launch_tile<FA, FB, 256, 256>(a1, st);
-            if (e != hipSuccess) return e;
-            return launch_tile<FA, FB, 128, 256>(a2, st);
-        }
-    }
-    return launch_tile<FA, FB, 256, 256>(a, st);
-}
-
 hipError_t launch_scaled_gemm(const GemmArgs& a, hipStream_t st) {
+    if (a.precise) {
+        switch (a.fa * 3 + a.fb) {
+        case E4M3 * 3 + E4M3: return launch_t<E4M3, E4M3, true>(a, st);
+        case E4M3 * 3 + E5M2: return launch_t<E4M3, E5M2, true>(a, st);
+        case E5M2 * 3 + E4M3: return launch_t<E5M2, E4M3, true>(a, st);
+        case E5M2 * 3 + E5M2: return launch_t<E5M2, E5M2, true>(a, st);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (a.fa * 3 + a.fb) {
-    case E4M3 * 3 + E4M3: return launch_t<E4M3, E4M3>(a, st);
-    case E4M3 * 3 + E5M2: return launch_t<E4M3, E5M2>(a, st);
-    case E4M3 * 3 + E2M1: return launch_t<E4M3, E2M1>(a, st);
-    case E5M2 * 3 + E4M3: return launch_t<E5M2, E4M3>(a, st);
-    case E5M2 * 3 + E5M2: return launch_t<E5M2, E5M2>(a, st);
-    case E5M2 * 3 + E2M1: return launch_t<E5M2, E2M1>(a, st);
-    case E2M1 * 3 + E4M3: return launch_t<E2M1, E4M3>(a, st);
-    case E2M1 * 3 + E5M2: return launch_t<E2M1, E5M2>(a, st);
-    case E2M1 * 3 + E2M1: return launch_t<E2M1, E2M1>(a, st);
+    case E4M3 * 3 + E4M3: return launch_t<E4M3, E4M3, false>(a, st);
+    case E4M3 * 3 + E5M2: return launch_t<E4M3, E5M2, false>(a, st);
+    case E4M3 * 3 + E2M1: return launch_t<E4M3, E2M1, false>(a, st);
+    case E5M2 * 3 + E4M3: return launch_t<E5M2, E4M3, false>(a, st);
+    case E5M2 * 3 + E5M2: return launch_t<E5M2, E5M2, false>(a, st);
+    case E5M2 * 3 + E2M1: return launch_t<E5M2, E2M1, false>(a, st);
+    case E2M1 * 3 + E4M3: return launch_t<E2M1, E4M3, false>(a, st);
+    case E2M1 * 3 + E5M2: return launch_t<E2M1, E5M2, false>(a, st);
+    case E2M1 * 3 + E2M1: return launch_t<E2M1, E2M1, false>(a, st);
     }
     return hipErrorInvalidValue;
 }

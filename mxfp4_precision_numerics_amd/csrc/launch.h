@@ -38,5 +38,9 @@ struct GemmArgs {
     int precise;              // exact products (FP8 x FP8 only; E2M1 x E2M1 is exact natively)
 };
 hipError_t launch_scaled_gemm(const GemmArgs& a, hipStream_t st);
+// The launcher for one operand-format pair and mode (gemm_kernel.h;
+// instantiated by gemm_inst.hip).
+template <int FA, int FB, bool PRECISE>
+hipError_t launch_t(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mxq
