@@ -77,7 +77,7 @@ def main():
         sys.exit(2)
     import torch
     import mxfp4_precision_numerics_amd as mxq
-    from mxfp4_precision_numerics_amd import synth
+    import synth
 
     assert torch.cuda.is_available(), "bench.py needs the MI355X"
     mxq.lib()

@@ -20,7 +20,7 @@ Run ``python -m oracle.error_study`` for the table of the full-size samples.
 import numpy as np
 
 import oracle as O
-from mxfp4_precision_numerics_amd import synth
+import synth
 
 
 def _finite_f32(x):

@@ -14,7 +14,7 @@ import torch
 
 import oracle as O
 import mxfp4_precision_numerics_amd as mxq
-from mxfp4_precision_numerics_amd import synth
+import synth
 from gpu_helpers import (check_gemm, check_swiglu_codes, dev_bf16, dev_u8, empty_u8, host, mfma_bound,
                          require_gpu)
 

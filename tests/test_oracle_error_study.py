@@ -17,7 +17,7 @@ import numpy as np
 
 import oracle as O
 from oracle import error_study as ES
-from mxfp4_precision_numerics_amd import synth
+import synth
 
 
 def test_error_bounds_on_workload_samples():
