@@ -334,7 +334,8 @@ def rows_c4(ctx, rows):
     """Workload 4: one GPU's share of a 671B-class MoE: MXFP4 quantize,
     gather + repack, grouped expert GEMM; the expert MLP's activation and
     down-projection."""
-    ids = ("c4_mx_e2m1", "c4_repack", "c4_fp4col", "c4_grouped", "c4_grouped_fp4", "c4_swiglu", "c4_down")
+    ids = ("c4_mx_e2m1", "c4_repack", "c4_fp4col", "c4_grouped", "c4_up_swiglu_fused", "c4_grouped_fp4",
+           "c4_swiglu", "c4_down")
     if not any(ctx.want(i) for i in ids):
         return
     torch, mxq, synth = ctx.torch, ctx.mxq, ctx.synth
@@ -362,10 +363,21 @@ def rows_c4(ctx, rows):
     del x
     off_d = torch.from_numpy(off).to(ctx.dev)
     Cg = torch.empty((R, 4096), dtype=torch.bfloat16, device=ctx.dev)
-    if any(ctx.want(i) for i in ("c4_grouped", "c4_swiglu", "c4_down")):
+    if any(ctx.want(i) for i in ("c4_grouped", "c4_up_swiglu_fused", "c4_swiglu", "c4_down")):
         qw, sw = ctx.u8(32, 4096, 7168), ctx.u8(32, 4096, 224)
         for e in range(32):
             mxq.quantize_mx(ctx.bf16(synth.c4_w(e)), mxq.E4M3, qw[e], sw[e])
+        if ctx.want("c4_up_swiglu_fused"):
+            qhf, shf = ctx.u8(R, 2048), ctx.u8(R, 64)
+            t = ctx.timed(lambda: mxq.grouped_gemm_swiglu_quantize_mx(
+                q8, mxq.E4M3, s8, mxq.SCALE_BLK128, qw, mxq.E4M3, sw, mxq.SCALE_BLK32, off_d, 32, R, 2048, 7168,
+                mxq.E4M3, qhf, shf))
+            rows["c4_up_swiglu_fused"] = ctx.fl(
+                f"f2 expert up-projection with SwiGLU + MX E4M3 in the epilogue (gate/up never stored), 32 "
+                f"experts, R={R}, inter=2048, K=7168, block-scaled FP8 MFMA", 2.0 * R * 4096 * 7168, t,
+                FP8_PEAK_TFLOPS, True,
+                nbytes=32 * 4096 * 7168 * (1 + 1 / 32) + R * 7168 * (1 + 1 / 128) + R * 2048 * (1 + 1 / 32))
+            del qhf, shf
 
         def grouped():
             mxq.grouped_scaled_gemm(q8, mxq.E4M3, s8, mxq.SCALE_BLK128, qw, mxq.E4M3, sw, mxq.SCALE_BLK32, off_d,

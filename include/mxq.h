@@ -261,6 +261,45 @@ int mxq_grouped_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, co
                             const void* sB, int mb, const int64_t* group_off, int64_t G, int64_t total_rows,
                             int64_t N, int64_t K, void* C, int out, void* stream);
 
+/*
+ * mxq_grouped_gemm_swiglu_quantize_mx - the expert MLP's up-projection with
+ * its activation fused into the GEMM's epilogue: for every group g and every
+ * row m of it, the gate and up projections gate = deq(A_m) . deq(B_g[c])^T
+ * and up = deq(A_m) . deq(B_g[inter + c])^T (fp32 accumulation as
+ * mxq_grouped_scaled_gemm, block-scaled FP8 MFMA), h = silu(gate) * up with
+ * silu(x) = x / (1 + e^-x) formed in binary32, and h MX block-32 quantized
+ * along the intermediate dimension as mxq_swiglu_quantize_mx does.  The
+ * gate/up output never reaches memory.
+ *
+ * Defines: [MoE FP4], "Metodologia" (the expert GEMMs run in FP8 on ragged
+ * per-expert rows; the activation between the two expert GEMMs is
+ * requantized to FP8 for the down-projection) and "Kernels CUDA Otimizados"
+ * (ragged per-expert token counts).  The pages do not name the activation;
+ * this library reads it as SwiGLU (see mxq_swiglu_quantize_mx).
+ *  A, sA, ma  [total_rows, K] FP8 codes (E4M3 or E5M2) with scales as in
+ *             mxq_scaled_gemm (per-tensor, BLK32 or BLK128)
+ *  B, sB, mb  [G, 2 inter, K] FP8 codes: rows 0 .. inter-1 of each group are
+ *             the gate projection's weights, rows inter .. 2 inter - 1 the up
+ *             projection's (the layout of the plain grouped GEMM's B for
+ *             N = 2 inter); scales [G, 2 inter, K/32] or [G, 2 inter, K/128],
+ *             or one float for MXQ_SCALE_TENSOR
+ *  group_off  DEVICE int64[G+1], as mxq_grouped_scaled_gemm (clamped to
+ *             [0, total_rows] on the device)
+ *  hfmt       MXQ_E4M3 or MXQ_E5M2: the format of h
+ *  q_out      [total_rows, inter] codes of h (16-byte aligned); rows outside
+ *             every group are not written
+ *  s_out      [total_rows, inter/32] E8M0 scale bytes of h
+ * h comes from the fp32 accumulators, so a code may differ from one computed
+ * on the exact sums where h lies within the GEMM's rounding of a rounding
+ * boundary (see mxq_scaled_gemm for what the FP8 MFMA rounds).
+ * Rules: inter % 128 == 0, K % 128 == 0; A and each group's B below 4 GiB;
+ * G <= 4096; FP8 operands only (E2M1 -> MXQ_ERR_FORMAT).
+ */
+int mxq_grouped_gemm_swiglu_quantize_mx(const uint8_t* A, int fa, const void* sA, int ma, const uint8_t* B, int fb,
+                                        const void* sB, int mb, const int64_t* group_off, int64_t G,
+                                        int64_t total_rows, int64_t inter, int64_t K, int hfmt, uint8_t* q_out,
+                                        uint8_t* s_out, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* mxq_status_string(int status);
 

@@ -56,6 +56,9 @@ def lib():
         L.mxq_scaled_gemm.argtypes = [p, i, p, i, p, i, p, i, i64, i64, i64, p, i, i64, p]
         L.mxq_grouped_scaled_gemm.restype = i
         L.mxq_grouped_scaled_gemm.argtypes = [p, i, p, i, p, i, p, i, p, i64, i64, i64, i64, p, i, p]
+        L.mxq_grouped_gemm_swiglu_quantize_mx.restype = i
+        L.mxq_grouped_gemm_swiglu_quantize_mx.argtypes = [p, i, p, i, p, i, p, i, p, i64, i64, i64, i64, i, p, p,
+                                                          p]
         _lib = L
     return _lib
 
@@ -308,6 +311,27 @@ def grouped_scaled_gemm(A, fa, sA, ma, B, fb, sB, mb, group_off, G, total_rows, 
     st = L.mxq_grouped_scaled_gemm(_ptr(A), fa, _ptr(sA), ma, _ptr(B), fb, _ptr(sB), mb, _ptr(group_off), G,
                                    total_rows, N, K, _ptr(C), out, _stream(stream))
     _check("mxq_grouped_scaled_gemm", st)
+
+
+def grouped_gemm_swiglu_quantize_mx(A, fa, sA, ma, B, fb, sB, mb, group_off, G, total_rows, inter, K, hfmt, q,
+                                    s, stream=None):
+    """Expert up-projection with the SwiGLU + MX epilogue
+    (mxq_grouped_gemm_swiglu_quantize_mx).  B [G, 2 inter, K] holds each
+    group's gate rows then its up rows; q [total_rows, inter] and s
+    [total_rows, inter/32] receive h = silu(gate) * up, MX quantized."""
+    L = lib()
+    import torch
+    _buf("A", A, _u8(), total_rows * K)
+    _buf("B", B, _u8(), G * 2 * inter * K)
+    _scale("sA", sA, ma, total_rows, K)
+    _scale("sB", sB, mb, G * 2 * inter if mb != SCALE_TENSOR else 1, K)
+    _buf("group_off", group_off, (torch.int64,), G + 1)
+    _buf("q", q, _u8(), total_rows * inter)
+    _buf("s", s, _u8(), total_rows * (inter // 32))
+    _on_gpu(A=A, sA=sA, B=B, sB=sB, group_off=group_off, q=q, s=s)
+    st = L.mxq_grouped_gemm_swiglu_quantize_mx(_ptr(A), fa, _ptr(sA), ma, _ptr(B), fb, _ptr(sB), mb, _ptr(group_off),
+                                               G, total_rows, inter, K, hfmt, _ptr(q), _ptr(s), _stream(stream))
+    _check("mxq_grouped_gemm_swiglu_quantize_mx", st)
 
 
 # --------------------------------------------------------------------------

@@ -164,6 +164,40 @@ __device__ __forceinline__ uint32_t cast2_sat_f32(float y0, float y1) {
     return r;
 }
 
+// --- MX block codes and the expert MLP activation ------------------------------
+// Codes and scale byte of 8 binary32 values (bit patterns) of one 32-element
+// MX block whose largest magnitude (bit pattern, NaN/Inf included) is
+// amax_bits: e = floor(log2 amax) - emax clamped at -127, each value clamped
+// to the largest finite magnitude at that scale (saturation) and converted by
+// the scaled RNE converter; a block holding NaN or Inf gets codes 0x7F and
+// scale byte 0xFF.
+template <int F>
+__device__ __forceinline__ void mx_codes_row8(const uint32_t (&u)[8], uint32_t amax_bits, uint32_t& lo, uint32_t& hi,
+                                              uint8_t& sbyte) {
+    const bool bad = amax_bits >= 0x7F800000u;
+    const int e = block_exp<F>(amax_bits >> 23);
+    const float sc = exp2i(e);
+    const uint32_t lim = (uint32_t)(e + 127 + FmtInfo<F>::emax) << 23 | FmtInfo<F>::max_mant_f32;
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = as_float(clamp_f32(u[k], lim));
+    lo = cvt2_f32_fp8<F>(0u, y[0], y[1], sc, false);
+    lo = cvt2_f32_fp8<F>(lo, y[2], y[3], sc, true);
+    hi = cvt2_f32_fp8<F>(0u, y[4], y[5], sc, false);
+    hi = cvt2_f32_fp8<F>(hi, y[6], y[7], sc, true);
+    if (bad) { lo = 0x7F7F7F7Fu; hi = 0x7F7F7F7Fu; }
+    sbyte = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
+}
+
+// h = silu(g) * u in binary32, silu(g) = g / (1 + e^-g): the sigmoid from
+// e^-|g| in (0, 1], which cannot overflow (very negative gates keep their
+// subnormal products instead of 0), and the hardware reciprocal (1 ulp).
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+    const float en = expf(-__builtin_fabsf(g));
+    const float sg = (g >= 0.0f ? 1.0f : en) * __builtin_amdgcn_rcpf(1.0f + en);
+    return g * sg * u;
+}
+
 // --- streaming memory access ----------------------------------------------------
 // The casts read every input once and write every output once.  They use
 // nontemporal loads and stores (the instructions' nt cache policy), which

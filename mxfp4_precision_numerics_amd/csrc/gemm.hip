@@ -29,4 +29,14 @@ hipError_t launch_scaled_gemm(const GemmArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_grouped_swiglu(const GemmArgs& a, hipStream_t st) {
+    switch (a.fa * 3 + a.fb) {
+    case E4M3 * 3 + E4M3: return launch_swiglu_t<E4M3, E4M3>(a, st);
+    case E4M3 * 3 + E5M2: return launch_swiglu_t<E4M3, E5M2>(a, st);
+    case E5M2 * 3 + E4M3: return launch_swiglu_t<E5M2, E4M3>(a, st);
+    case E5M2 * 3 + E5M2: return launch_swiglu_t<E5M2, E5M2>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace mxq

@@ -10,4 +10,8 @@
 
 namespace mxq {
 template hipError_t launch_t<MXQ_FA, MXQ_FB, (MXQ_PRECISE != 0)>(const GemmArgs&, hipStream_t);
+#if MXQ_PRECISE == 0 && MXQ_FA != 2 && MXQ_FB != 2
+// FP8 x FP8: also the up-projection with the SwiGLU + MX epilogue
+template hipError_t launch_swiglu_t<MXQ_FA, MXQ_FB>(const GemmArgs&, hipStream_t);
+#endif
 }  // namespace mxq

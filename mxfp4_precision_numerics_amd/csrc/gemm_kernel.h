@@ -185,28 +185,43 @@ __device__ __forceinline__ void dma16(const v4u& rsrc, uint32_t voff, uint32_t s
 // unit that can run past the end of a row (FP4 x FP4 units of two K steps
 // when K % 256 == 128) must be range-checked on the last row, so there the
 // unit's offset is added to the per-lane offset.
-template <int RB, int ROWS, bool LANE_UNIT = false>
+//
+// GU (gate/up tiles of the expert MLP, 256 rows of 128 bytes): tile rows
+// [64b, 64b + 64) come from operand rows row0 + 64 (b / 2) + .. of the gate
+// half for even b and of the up half (gu bytes further) for odd b, so that a
+// tile holds gate and up rows of the same 128 intermediate columns, the gate
+// rows of each 64 followed by the up rows of the same 64.  Piece i (8 rows)
+// lies in block i / 2 at rows 32 (i % 2) .. of it.
+template <int RB, int ROWS, bool LANE_UNIT = false, bool GU = false>
 struct TileLoader {
     static constexpr int CH = RB / 16;
     static constexpr int PER_WAVE = ROWS * RB / 1024 / 4;
     static constexpr int RP = 1024 / RB;  // rows per 1 KiB piece
     static_assert(PER_WAVE >= 1 && ROWS * RB % 4096 == 0, "tile unit must split over 4 waves");
+    static_assert(!GU || (RB == 128 && ROWS == 256), "gate/up tiles are 256 rows of 128 bytes");
     v4u rsrc;
-    uint32_t off0, step;  // lane offset of piece 0; bytes between pieces
+    uint32_t off0, step, gu;  // lane offset of piece 0; bytes between pieces; gate -> up
     __device__ __forceinline__ void init(const uint8_t* base, int64_t bytes, int64_t ld, int64_t row0, int wave,
-                                         int lane) {
+                                         int lane, int64_t gu_rows = 0) {
         rsrc = make_rsrc(base, bytes);
         const int o = wave * 1024 + lane * 16;
         const int r = o / RB, p = (o % RB) / 16;
         off0 = (uint32_t)((row0 + r) * ld + ((p ^ swz<RB>(r)) << 4));
         step = (uint32_t)(4 * RP * ld);
+        gu = (uint32_t)(gu_rows * ld);
+    }
+    __device__ __forceinline__ uint32_t piece(int i) const {
+        if constexpr (GU)
+            return (uint32_t)(2 * (i / 4) + (i % 2)) * step + (uint32_t)((i / 2) & 1) * gu;
+        else
+            return (uint32_t)i * step;
     }
     __device__ __forceinline__ void issue(int i, int64_t unit, uint32_t slot, int wave) const {
         const uint32_t u = (uint32_t)(unit * RB), dst = slot + (uint32_t)(wave + 4 * i) * 1024u;
         if constexpr (LANE_UNIT)
-            dma16(rsrc, off0 + (uint32_t)i * step + u, 0u, dst);
+            dma16(rsrc, off0 + piece(i) + u, 0u, dst);
         else
-            dma16(rsrc, off0 + (uint32_t)i * step, u, dst);
+            dma16(rsrc, off0 + piece(i), u, dst);
     }
 };
 
@@ -221,22 +236,25 @@ struct TileLoader {
 // not wholly inside the range, so a BLK128 array whose size is not a multiple
 // of 4 gets a range rounded up to the end of its last aligned dword: the last
 // row's bytes arrive, the (unused) padding bytes share that dword's page.
+// GU: the tile rows of TileLoader's gate/up mode (wave w copies block w).
 constexpr int SG = 4;
-template <int ROWS>
+template <int ROWS, bool GU = false>
 struct ScaleLoader {
     static_assert(ROWS == 128 || ROWS == 256, "scale rows");
+    static_assert(!GU || ROWS == 256, "gate/up tiles are 256 rows");
     v4u rsrc;
     uint32_t off, kmul, mask;
     int dst;  // byte offset of this wave's 64 rows within the operand's part of the slot
     __device__ __forceinline__ void init(int mode, const void* s, int64_t K, int64_t rows, int64_t row0, int wave,
-                                         int lane) {
+                                         int lane, int64_t gu_rows = 0) {
         const int64_t pitch = (mode == 1) ? K / 32 : (mode == 2 ? K / 128 : 0);
         kmul = mode == 1 ? 4u : (mode == 2 ? 1u : 0u);
         mask = mode == 2 ? ~3u : ~0u;
         rsrc = make_rsrc(s, mode == 0 ? 4 : (rows * pitch + 3) & ~(int64_t)3);
         const int r = (wave * 64) % ROWS;
         dst = r * 16;
-        off = (uint32_t)((row0 + r + lane) * pitch);
+        const int64_t grow = GU ? row0 + 64 * (wave / 2) + (wave % 2) * gu_rows : row0 + r;
+        off = (uint32_t)((grow + lane) * pitch);
     }
     __device__ __forceinline__ void issue(int64_t grp, uint32_t slot) const {
         dma16(rsrc, (off + (uint32_t)(grp * SG) * kmul) & mask, 0u, slot + (uint32_t)dst);
@@ -291,9 +309,18 @@ constexpr int copies_after(int J, int NSL, int SU, int TL, int JS) {
 // bf16's range), then v_mfma_f32_32x32x16_bf16 accumulates the exact
 // products in fp32.  Slower than the block-scaled FP8 MFMA, whose products
 // are truncated to 13 fractional bits inside each run of 8 K positions.
-template <int FA, int FB, int BM, int BN, bool PRECISE = false>
+//
+// HF >= 0 (the expert MLP's up-projection; grouped, FP8 operands, BN = 256):
+// B tiles hold gate and up rows of 128 intermediate columns (TileLoader's GU
+// mode), so each wave's accumulators hold gate in fragments 0, 1 and up of
+// the same columns in 2, 3 (same lanes, same registers).  The epilogue forms
+// h = silu(gate) * up in binary32 and writes h MX block-32 quantized to
+// format HF (q_out, s_out) instead of C.
+template <int FA, int FB, int BM, int BN, bool PRECISE = false, int HF = -1>
 __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     static_assert(!PRECISE || (FA != E2M1 && FB != E2M1), "precise mode takes FP8 operands");
+    constexpr bool GU = HF >= 0;
+    static_assert(!GU || (BN == 256 && FA != E2M1 && FB != E2M1 && !PRECISE), "gate/up epilogue configuration");
     using IA = OpInfo<FA>;
     using IB = OpInfo<FB>;
     // Ring unit: SU K halves.  Copies fetch RB contiguous bytes per row, and
@@ -348,15 +375,18 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     // FP4 x FP4 units are two K steps: the last one may run past a row's end
     constexpr bool LU = SU > 2;
     TileLoader<RBA, BM, LU> ldA;
-    TileLoader<RBB, BN, LU> ldB;
+    TileLoader<RBB, BN, LU, GU> ldB;
+    // gate/up tiles: tile n0 (a multiple of 256) covers intermediate columns
+    // n0 / 2 .. + 127, gate rows from n0 / 2, up rows inter further
+    const int64_t b_row0 = GU ? t.n0 / 2 : t.n0;
     ldA.init(g.A, g.M * lda, lda, t.m0, wave, lane);
-    ldB.init(t.B, g.N * ldb, ldb, t.n0, wave, lane);
+    ldB.init(t.B, g.N * ldb, ldb, b_row0, wave, lane, g.inter);
     ScaleLoader<BM> lsA;
-    ScaleLoader<BN> lsB;
+    ScaleLoader<BN, GU> lsB;
     lsA.init(g.ma, g.sA, g.K, g.M, t.m0, wave, lane);
-    lsB.init(g.mb, t.sB, g.K, g.N, t.n0, wave, lane);
+    lsB.init(g.mb, t.sB, g.K, g.N, b_row0, wave, lane, g.inter);
     constexpr int TLA = TileLoader<RBA, BM, LU>::PER_WAVE;
-    constexpr int TL = TLA + TileLoader<RBB, BN, LU>::PER_WAVE;  // tile copies per unit
+    constexpr int TL = TLA + TileLoader<RBB, BN, LU, GU>::PER_WAVE;  // tile copies per unit
 
     // Scale operand of a fragment row, from the staged dword: the byte for K
     // half h ends up at byte 2h (BLK32: blocks 2h + gq; BLK128: the step's
@@ -711,10 +741,59 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
                 __syncthreads();
             }
     };
-    if (g.out == 0)
+    if constexpr (GU) {
+        // Expert MLP epilogue.  The wave's 64 intermediate columns: fragment
+        // jj < 2 of a row band holds gate columns 32 jj + l % 32, jj + 2 the
+        // up values of the same columns.  Per 32-row band: h in binary32 is
+        // staged in the wave's LDS room (rows of 64 floats, padded by 4), then
+        // read back 8 consecutive columns per lane, so that a quad of lanes
+        // holds one MX block of 32 (the same arithmetic as the standalone
+        // activation kernel on binary32 input).
+        static_assert(FN == 4, "gate and up fragments");
+        constexpr int HP = 68;  // floats per staged row
+        static_assert(32 * HP * 4 <= CAP, "epilogue band");
+        float* band = reinterpret_cast<float*>(mine);
+        const int64_t hcol = t.n0 / 2 + wn * 64;  // first intermediate column of the wave
+        const int64_t spr = g.inter / 32;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    band[(8 * (r / 4) + 4 * gq + (r % 4)) * HP + 32 * jj + (lane & 31)] =
+                        swiglu_f32(acc[i][jj][r] * alpha, acc[i][jj + 2][r] * alpha);
+            __syncthreads();
+#pragma unroll
+            for (int pass = 0; pass < 4; ++pass) {
+                const int br = 8 * pass + lane / 8, ch = lane % 8;
+                const float* src = band + br * HP + 8 * ch;
+                const uint4 a = *reinterpret_cast<const uint4*>(src), b = *reinterpret_cast<const uint4*>(src + 4);
+                const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                uint32_t m = 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t v = u[k] & 0x7FFFFFFFu;
+                    m = m > v ? m : v;
+                }
+                m = quad_max_u32(m);  // lanes 4q .. 4q+3: one row's 32-column block
+                uint32_t lo, hi;
+                uint8_t sb;
+                mx_codes_row8<HF>(u, m, lo, hi, sb);
+                const int rr = 32 * i + br;
+                if (rr < mlim) {
+                    const int64_t row = row_base + rr;
+                    *reinterpret_cast<uint2*>(g.q_out + row * g.inter + hcol + 8 * ch) = make_uint2(lo, hi);
+                    if ((lane & 3) == 0) g.s_out[row * spr + (hcol + 8 * ch) / 32] = sb;
+                }
+            }
+            __syncthreads();
+        }
+    } else if (g.out == 0) {
         store_tile(float{});
-    else
+    } else {
         store_tile(uint16_t{});
+    }
 }
 
 // Compute units of the current device (queried once per process).
@@ -731,12 +810,24 @@ inline int64_t cu_count() {
     return n;
 }
 
-template <int FA, int FB, int BM, int BN, bool PRECISE>
+template <int FA, int FB, int BM, int BN, bool PRECISE, int HF = -1>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
     const int64_t ntn = (a.N + BN - 1) / BN;
     const int64_t ntm = (a.group_off == nullptr) ? (a.M + BM - 1) / BM : (a.M + BM - 1) / BM + a.G;
-    hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE>), dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE, HF>), dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a);
     return hipGetLastError();
+}
+
+// The expert MLP's up-projection with the SwiGLU + MX epilogue (grouped, FP8
+// operands, native mode): 256-row tiles once the groups average 192 rows.
+template <int FA, int FB>
+hipError_t launch_swiglu_t(const GemmArgs& a, hipStream_t st) {
+    const int64_t rows = a.M / (a.G > 0 ? a.G : 1);
+    if (a.hfmt == E5M2)
+        return rows < 192 ? launch_tile<FA, FB, 128, 256, false, E5M2>(a, st)
+                          : launch_tile<FA, FB, 256, 256, false, E5M2>(a, st);
+    return rows < 192 ? launch_tile<FA, FB, 128, 256, false, E4M3>(a, st)
+                      : launch_tile<FA, FB, 256, 256, false, E4M3>(a, st);
 }
 
 // Tile choice: the largest tiles (most operand reuse per LDS byte) unless

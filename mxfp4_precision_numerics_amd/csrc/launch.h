@@ -36,11 +36,25 @@ struct GemmArgs {
     int64_t sb_group_stride; // bytes between consecutive sB_g (0 for per-tensor)
     int fa, fb, ma, mb, out;  // out: 0 fp32, 1 bf16
     int precise;              // exact products (FP8 x FP8 only; E2M1 x E2M1 is exact natively)
+    // Expert-MLP epilogue (C unused): B_g = [gate rows 0..inter-1; up rows
+    // inter..2 inter-1], N = 2 inter; each output row's h = silu(gate) * up
+    // is MX block-32 quantized to q_out [M, inter] with scales s_out
+    // [M, inter/32] in format hfmt.
+    int swiglu;
+    int hfmt;
+    int64_t inter;
+    uint8_t* q_out;
+    uint8_t* s_out;
 };
 hipError_t launch_scaled_gemm(const GemmArgs& a, hipStream_t st);
+// Grouped up-projection with the SwiGLU + MX epilogue (a.swiglu set).
+hipError_t launch_grouped_swiglu(const GemmArgs& a, hipStream_t st);
 // The launcher for one operand-format pair and mode (gemm_kernel.h;
 // instantiated by gemm_inst.hip).
 template <int FA, int FB, bool PRECISE>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st);
+// The grouped GEMM with the SwiGLU + MX epilogue, FP8 operands.
+template <int FA, int FB>
+hipError_t launch_swiglu_t(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mxq

@@ -187,4 +187,32 @@ int mxq_grouped_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, co
     return hip_status(mxq::launch_scaled_gemm(a, as_stream(stream)));
 }
 
+int mxq_grouped_gemm_swiglu_quantize_mx(const uint8_t* A, int fa, const void* sA, int ma, const uint8_t* B, int fb,
+                                        const void* sB, int mb, const int64_t* group_off, int64_t G,
+                                        int64_t total_rows, int64_t inter, int64_t K, int hfmt, uint8_t* q_out,
+                                        uint8_t* s_out, void* stream) {
+    if (G < 0 || G > 4096 || total_rows < 0 || inter < 0) return MXQ_ERR_SHAPE;
+    if (fa == MXQ_E2M1 || fb == MXQ_E2M1) return MXQ_ERR_FORMAT;
+    if (hfmt != MXQ_E4M3 && hfmt != MXQ_E5M2) return MXQ_ERR_FORMAT;
+    // the operand checks of the plain GEMM, with q_out in the place of C
+    const int st = check_operands(A, fa, sA, ma, B, fb, sB, mb, K, q_out, MXQ_OUT_F32);
+    if (st != MXQ_OK) return st;
+    if (!group_off || !s_out) return MXQ_ERR_NULL;
+    if (!aligned4(group_off)) return MXQ_ERR_ALIGN;
+    if (inter % 128 != 0) return MXQ_ERR_SHAPE;
+    if (G == 0 || total_rows == 0 || inter == 0) return MXQ_OK;
+    const int64_t N = 2 * inter;
+    if (((total_rows + 127) / 128 + G) * ((N + 255) / 256) > MAX_GRID_X) return MXQ_ERR_SHAPE;
+    if (!below_4gib(total_rows, K, fa, ma) || !below_4gib(N, K, fb, mb)) return MXQ_ERR_SHAPE;
+    mxq::GemmArgs a{};
+    a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = nullptr;
+    a.group_off = group_off; a.G = G;
+    a.M = total_rows; a.N = N; a.K = K; a.ldc = N;
+    a.b_group_stride = N * K;
+    a.sb_group_stride = mb == MXQ_SCALE_BLK32 ? N * (K / 32) : (mb == MXQ_SCALE_BLK128 ? N * (K / 128) : 0);
+    a.fa = fa; a.fb = fb; a.ma = ma; a.mb = mb; a.out = MXQ_OUT_F32;
+    a.swiglu = 1; a.hfmt = hfmt; a.inter = inter; a.q_out = q_out; a.s_out = s_out;
+    return hip_status(mxq::launch_grouped_swiglu(a, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -439,24 +439,6 @@ __global__ void __launch_bounds__(MXR_THREADS) k_mx_row(const void* __restrict__
 // quad (lane bits 0-1).  Column phase: a 32-row block spans the 4 lanes that
 // differ in lane bits 2-3.
 // ---------------------------------------------------------------------------
-template <int F>
-__device__ __forceinline__ void mx_codes_row8(const uint32_t (&u)[8], uint32_t amax_bits, uint32_t& lo, uint32_t& hi,
-                                              uint8_t& sbyte) {
-    const bool bad = amax_bits >= 0x7F800000u;
-    const int e = block_exp<F>(amax_bits >> 23);
-    const float sc = exp2i(e);
-    const uint32_t lim = (uint32_t)(e + 127 + FmtInfo<F>::emax) << 23 | FmtInfo<F>::max_mant_f32;
-    float y[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] = as_float(clamp_f32(u[k], lim));
-    lo = cvt2_f32_fp8<F>(0u, y[0], y[1], sc, false);
-    lo = cvt2_f32_fp8<F>(lo, y[2], y[3], sc, true);
-    hi = cvt2_f32_fp8<F>(0u, y[4], y[5], sc, false);
-    hi = cvt2_f32_fp8<F>(hi, y[6], y[7], sc, true);
-    if (bad) { lo = 0x7F7F7F7Fu; hi = 0x7F7F7F7Fu; }
-    sbyte = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
-}
-
 template <int F, int SRC>
 __global__ void __launch_bounds__(256) k_mx_dual(const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
                                                  uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
@@ -592,13 +574,7 @@ __global__ void __launch_bounds__(256) k_swiglu_mx(const void* __restrict__ gu, 
         uint32_t m = 0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            // sigma(g) from e^-|g| in (0, 1], which cannot overflow: very
-            // negative gates keep their (subnormal) products instead of 0
-            const float g = as_float(gw[it][k]);
-            const float en = expf(-__builtin_fabsf(g));
-            const float sg = (g >= 0.0f ? 1.0f : en) * __builtin_amdgcn_rcpf(1.0f + en);  // rcp: 1 ulp
-            const float y = g * sg * as_float(uw[it][k]);
-            h[k] = as_uint(y);
+            h[k] = as_uint(swiglu_f32(as_float(gw[it][k]), as_float(uw[it][k])));
             const uint32_t a = h[k] & 0x7FFFFFFFu;
             m = m > a ? m : a;
         }

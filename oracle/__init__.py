@@ -321,6 +321,26 @@ def grouped_gemm_entries(A, fa, sA, ma, B, fb, sB, mb, off, N, K, m_idx, n_idx):
     return c, cabs
 
 
+def expert_up_swiglu_mx(A, fa, sA, ma, B, fb, sB, mb, off, inter, K, rows, hfmt):
+    """The expert MLP's up-projection followed by its activation step, for
+    the listed rows of A ([MoE FP4] "Metodologia": the expert GEMMs in FP8,
+    the activation between them requantized; activation read as SwiGLU):
+    gate and up = the grouped GEMM (O9, fp64 sums of exact products) over the
+    2 inter columns of each row's group (gate columns [0, inter), up
+    [inter, 2 inter)), then h = silu(gate) * up in fp64 and MX block-32
+    quantization of h (O6).  Rows must lie in a group.  Returns (q [n, inter],
+    s [n, inter/32], h [n, inter], gu [n, 2 inter], gu_abs [n, 2 inter]), the
+    last being sum |a||b| of each gate/up entry."""
+    rows = np.asarray(rows, np.int64)
+    N = 2 * inter
+    m_idx = np.repeat(rows, N)
+    n_idx = np.tile(np.arange(N, dtype=np.int64), len(rows))
+    c, cabs = grouped_gemm_entries(A, fa, sA, ma, B, fb, sB, mb, off, N, K, m_idx, n_idx)
+    gu = c.reshape(len(rows), N)
+    q, s, h = swiglu_quantize_mx(gu, inter, hfmt)
+    return q, s, h, gu, cabs.reshape(len(rows), N)
+
+
 def num_threads():
     """OpenMP threads the oracle's loops run on."""
     return int(lib().or_num_threads())

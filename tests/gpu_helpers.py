@@ -203,6 +203,69 @@ def gemm_scale_arg(s, mode):
     return dev_u8(s)
 
 
+def check_mx_codes_near(q, s, h, delta, fmt, what="", min_same=0.999, oq=None):
+    """MX block-32 codes q / scale bytes s of a GPU result against the exact
+    values h (float64 [rows, inter]) when the GPU's own h may be off by up to
+    delta per element: NaN/Inf blocks must be identical; elsewhere each block
+    exponent may be any the oracle's rule gives for amax -+ that error and
+    each code any code between those of (h -+ delta) / 2^e.  At least
+    `min_same` of the codes must equal the oracle's own (oq).  Returns the
+    shares of identical codes and scale bytes."""
+    import oracle as O
+    rows, inter = h.shape
+    nb = inter // 32
+    hb = h.reshape(rows, nb, 32)
+    bad = ~np.all(np.isfinite(hb), axis=2)
+    qb = q.reshape(rows, nb, 32)
+    assert np.all(s[bad] == 0xFF) and np.all(qb[bad] == 0x7F), f"{what}: NaN blocks"
+    delta = np.where(bad[:, :, None], 0.0, np.asarray(delta).reshape(hb.shape))
+    emax = O.emax(fmt)
+
+    def block_e(a):
+        e = np.full(a.shape, -127, np.int64)
+        pos = a > 0
+        e[pos] = np.floor(np.log2(a[pos])).astype(np.int64) - emax
+        return np.clip(e, -127, 127)
+
+    habs = np.abs(np.where(bad[:, :, None], 0.0, hb))
+    e_lo = block_e(np.maximum(habs - delta, 0).max(axis=2))
+    e_hi = block_e((habs + delta).max(axis=2))
+    eg = s.astype(np.int64) - 127
+    ok_e = bad | ((eg >= e_lo) & (eg <= e_hi))
+    assert ok_e.all(), f"{what}: {int((~ok_e).sum())} block exponents outside the bound"
+    tab = O.decode_table(fmt)
+    scale = np.exp2(-eg.astype(np.float64))[:, :, None]
+    hz = np.where(bad[:, :, None], 0.0, hb)
+    lo = O.cast_array(fmt, np.ascontiguousarray(((hz - delta) * scale).ravel())).reshape(hb.shape)
+    hi = O.cast_array(fmt, np.ascontiguousarray(((hz + delta) * scale).ravel())).reshape(hb.shape)
+    val, vlo, vhi = tab[qb], tab[lo], tab[hi]
+    ok = bad[:, :, None] | ((val >= vlo) & (val <= vhi))
+    assert ok.all(), f"{what}: {int((~ok).sum())} codes outside the bound"
+    if oq is None:
+        oq, os_, _, _ = O.quantize_mx(np.ascontiguousarray(h), fmt)
+    else:
+        os_ = None
+    same = float(np.mean(q == oq))
+    assert same >= min_same, f"{what}: only {same:.5f} of the codes bit-identical"
+    return same, (float(np.mean(s == os_)) if os_ is not None else None)
+
+
+def swiglu_delta(gu, gerr, inter, rel=2.0 ** -19):
+    """Bound on |h_gpu - h| for h = silu(gate) * up when the GPU's gate and
+    up are off by at most gerr (per element, [rows, 2 inter]) and h is then
+    formed in binary32 (relative rel, plus a few subnormal steps):
+    |silu'| <= 1.1, so |dh| <= 1.1 e_g (|u| + e_u) + (|silu(g)| + 1.1 e_g) e_u."""
+    import oracle as O
+    g, u = gu[:, :inter], gu[:, inter:2 * inter]
+    eg, eu = gerr[:, :inter], gerr[:, inter:2 * inter]
+    with np.errstate(invalid="ignore", over="ignore"):
+        sg = O.silu(g)
+        h = sg * u
+        d = 1.1 * eg * (np.abs(u) + eu) + (np.abs(sg) + 1.1 * eg) * eu + rel * np.abs(h)
+        d = d + 2.0 ** -146 * (1.0 + np.nan_to_num(np.abs(g * u), nan=0.0, posinf=0.0))
+    return np.nan_to_num(d, nan=0.0, posinf=0.0)
+
+
 def check_swiglu_codes(q, s, gu, inter, fmt, what="", rel=2.0 ** -19):
     """GPU codes/scales of mxq_swiglu_quantize_mx against the oracle, which
     forms h = silu(gate) * up in float64.  The kernel forms h in binary32 (a

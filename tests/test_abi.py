@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
 
@@ -146,6 +146,24 @@ def test_gemm_validation(L):
     assert gg(P, 0, P, 2, P, 0, P, 1, P, 5000, 64, 128, 128, P, 1, None) == ESHAPE
     assert gg(P, 0, P, 2, P, 0, P, 1, P, 0, 64, 128, 128, P, 1, None) == OK   # no groups
     assert gg(P, 0, P, 0, P, 0, P, 0, P, 4, 1 << 25, 128, 128, P, 1, None) == ESHAPE  # A 4 GiB
+
+
+def test_fused_expert_up_projection_validation(L):
+    f = L.mxq_grouped_gemm_swiglu_quantize_mx
+    # (A, fa, sA, ma, B, fb, sB, mb, off, G, rows, inter, K, hfmt, q, s, stream)
+    assert f(P, 2, P, 1, P, 0, P, 1, P, 4, 64, 128, 256, 0, P, P, None) == EFMT   # E2M1 operand
+    assert f(P, 0, P, 1, P, 2, P, 1, P, 4, 64, 128, 256, 0, P, P, None) == EFMT
+    assert f(P, 0, P, 1, P, 0, P, 1, P, 4, 64, 128, 256, 2, P, P, None) == EFMT   # h as E2M1
+    assert f(P, 0, P, 1, P, 0, P, 1, P, 4, 64, 96, 256, 0, P, P, None) == ESHAPE  # inter % 128
+    assert f(P, 0, P, 1, P, 0, P, 1, P, 4, 64, 128, 200, 0, P, P, None) == ESHAPE  # K % 128
+    assert f(P, 0, P, 1, P, 0, P, 1, P, 5000, 64, 128, 256, 0, P, P, None) == ESHAPE
+    assert f(P, 0, P, 1, P, 0, P, 1, None, 4, 64, 128, 256, 0, P, P, None) == ENULL
+    assert f(P, 0, P, 1, P, 0, P, 1, P, 4, 64, 128, 256, 0, P, None, None) == ENULL
+    assert f(P, 0, P, 1, P, 0, P, 1, P, 4, 64, 128, 256, 0, None, P, None) == ENULL
+    assert f(P, 0, P, 1, P, 0, P, 1, P, 4, 64, 128, 256, 0, P + 8, P, None) == EALIGN
+    assert f(P, 0, P, 1, P, 0, P, 1, P + 2, 4, 64, 128, 256, 0, P, P, None) == EALIGN
+    assert f(P, 0, P, 1, P, 0, P, 1, P, 4, 0, 128, 256, 0, P, P, None) == OK       # no rows
+    assert f(P, 0, P, 0, P, 0, P, 0, P, 4, 1 << 25, 128, 128, 0, P, P, None) == ESHAPE  # A 4 GiB
 
 
 def test_signatures_in_binding_match_header(L):

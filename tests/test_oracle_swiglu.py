@@ -90,3 +90,61 @@ def test_mx_float64_path_block_invariant():
         best = np.min(np.abs(finite[None, :] - clip.reshape(-1, 1)), axis=1).reshape(y.shape)
         assert np.allclose(np.abs(np.abs(got) - clip), best, rtol=0, atol=0)
         assert np.all((got == 0) | (np.sign(got) == np.sign(y)))
+
+
+def _fused_case(seed):
+    """Three groups (one empty) of MX E4M3 activations and gate/up weights."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    inter, K = 128, 256
+    sizes = [40, 0, 25]
+    off = np.zeros(4, np.int64)
+    off[1:] = np.cumsum(sizes)
+    R = int(off[-1])
+    xa = bf16_bits(g.standard_normal((R, K)).astype(np.float32))
+    A, sA, _, _ = O.quantize_mx(xa, O.E4M3)
+    Bs = [O.quantize_mx(bf16_bits(0.05 * g.standard_normal((2 * inter, K)).astype(np.float32)), O.E4M3)[:2]
+          for _ in range(3)]
+    B = np.stack([b for b, _ in Bs])
+    sB = np.stack([s for _, s in Bs])
+    return A, sA, B, sB, off, inter, K
+
+
+def test_expert_up_swiglu_is_gemm_then_activation():
+    """The fused expert step equals its two steps done apart: the dense GEMM
+    of each group's rows against that group's [gate; up] weights, then the
+    activation step on the float64 result."""
+    A, sA, B, sB, off, inter, K = _fused_case(11)
+    rows = np.array([0, 7, 39, 40, 64])
+    q, s, h, gu, gabs = O.expert_up_swiglu_mx(A, O.E4M3, sA, 1, B, O.E4M3, sB, 1, off, inter, K, rows, O.E4M3)
+    for k, r in enumerate(rows):
+        grp = int(np.searchsorted(off, r, side="right") - 1)
+        c, cab = O.gemm(A[r:r + 1], O.E4M3, sA[r:r + 1], 1, B[grp], O.E4M3, sB[grp], 1, 1, 2 * inter, K)
+        assert np.array_equal(gu[k], c[0]) and np.array_equal(gabs[k], cab[0])
+        q1, s1, h1 = O.swiglu_quantize_mx(c, inter, O.E4M3)
+        assert np.array_equal(q[k], q1[0]) and np.array_equal(s[k], s1[0]) and np.array_equal(h[k], h1[0])
+
+
+def test_expert_up_swiglu_gate_up_order():
+    """Gate rows are the first half of each group's weights: with identical
+    halves h = silu(x) x of the common projection x; exchanging the halves
+    changes h (silu(g) u != silu(u) g), and with the up half zero h is +-0."""
+    A, sA, B, sB, off, inter, K = _fused_case(12)
+    rows = np.arange(0, 65)
+    rows = rows[(rows < 40) | (rows >= 40)]
+    B2, sB2 = B.copy(), sB.copy()
+    B2[:, inter:], sB2[:, inter:] = B[:, :inter], sB[:, :inter]
+    _, _, h, gu, _ = O.expert_up_swiglu_mx(A, O.E4M3, sA, 1, B2, O.E4M3, sB2, 1, off, inter, K, rows, O.E4M3)
+    x = gu[:, :inter]
+    assert np.array_equal(gu[:, inter:], x)
+    assert np.allclose(h, x * x / (1.0 + np.exp(-x)), rtol=1e-15, atol=0)
+    Bs = B.copy()
+    Bs[:, :inter], Bs[:, inter:] = B[:, inter:], B[:, :inter]
+    sBs = sB.copy()
+    sBs[:, :inter], sBs[:, inter:] = sB[:, inter:], sB[:, :inter]
+    _, _, h0, _, _ = O.expert_up_swiglu_mx(A, O.E4M3, sA, 1, B, O.E4M3, sB, 1, off, inter, K, rows, O.E4M3)
+    _, _, hs, _, _ = O.expert_up_swiglu_mx(A, O.E4M3, sA, 1, Bs, O.E4M3, sBs, 1, off, inter, K, rows, O.E4M3)
+    assert not np.allclose(h0, hs)
+    Bz = B.copy()
+    Bz[:, inter:] = 0
+    qz, sz, hz, _, _ = O.expert_up_swiglu_mx(A, O.E4M3, sA, 1, Bz, O.E4M3, sB, 1, off, inter, K, rows, O.E4M3)
+    assert np.all(hz == 0) and np.all(sz == 0) and np.all((qz & 0x7F) == 0)
