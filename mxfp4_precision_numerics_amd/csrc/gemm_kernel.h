@@ -225,39 +225,50 @@ struct TileLoader {
     }
 };
 
-// Scale bytes of a group of SG = 4 K steps, 16 bytes per tile row (one copy
-// per wave).  BLK32: the row's 16 E8M0 bytes of the group's 16 32-blocks
-// (4-aligned since K % 128 == 0).  BLK128: the 16 bytes from the aligned
-// dword that holds the group's first byte, which covers the group's 4 bytes.
-// Per-tensor operands load from offset 0 of their float and never use the
-// data, so that every mode runs the same code.  With 128 rows, waves w and
-// w+2 copy the same rows.  Rows past the end read zero or the next group's
-// scales, as for the tiles.  The buffer range check drops any dword that is
-// not wholly inside the range, so a BLK128 array whose size is not a multiple
-// of 4 gets a range rounded up to the end of its last aligned dword: the last
-// row's bytes arrive, the (unused) padding bytes share that dword's page.
-// GU: the tile rows of TileLoader's gate/up mode (wave w copies block w).
+// Scale bytes of a group of SG = 4 K steps, 16 bytes per tile row, copied in
+// chunks of 64 rows (one copy each): NCH chunks over the 4 waves, NPW copies
+// per wave (a wave with no chunk of its own copies one again: identical bytes
+// to the same place).  BLK32: the row's 16 E8M0 bytes of the group's 16
+// 32-blocks (4-aligned since K % 128 == 0).  BLK128: the 16 bytes from the
+// aligned dword that holds the group's first byte, which covers the group's 4
+// bytes.  Per-tensor operands load from offset 0 of their float and never use
+// the data, so that every mode runs the same code.  Rows past the end read
+// zero or the next group's scales, as for the tiles.  The buffer range check
+// drops any dword that is not wholly inside the range, so a BLK128 array
+// whose size is not a multiple of 4 gets a range rounded up to the end of its
+// last aligned dword: the last row's bytes arrive, the (unused) padding bytes
+// share that dword's page.  GU: the tile rows of TileLoader's gate/up mode
+// (wave w copies block w).
 constexpr int SG = 4;
 template <int ROWS, bool GU = false>
 struct ScaleLoader {
-    static_assert(ROWS == 128 || ROWS == 256, "scale rows");
+    static constexpr int NCH = (ROWS + 63) / 64;     // chunks of 64 rows
+    static constexpr int NPW = (NCH + 3) / 4;        // copies per wave
+    static constexpr int SROWS = NCH * 64;           // rows of staging room
+    static_assert(ROWS % 32 == 0 && NCH >= 2, "scale rows");
     static_assert(!GU || ROWS == 256, "gate/up tiles are 256 rows");
     v4u rsrc;
-    uint32_t off, kmul, mask;
-    int dst;  // byte offset of this wave's 64 rows within the operand's part of the slot
+    uint32_t off[NPW], kmul, mask;
+    int dst[NPW];  // byte offsets of this wave's chunks within the operand's part of the slot
     __device__ __forceinline__ void init(int mode, const void* s, int64_t K, int64_t rows, int64_t row0, int wave,
                                          int lane, int64_t gu_rows = 0) {
         const int64_t pitch = (mode == 1) ? K / 32 : (mode == 2 ? K / 128 : 0);
         kmul = mode == 1 ? 4u : (mode == 2 ? 1u : 0u);
         mask = mode == 2 ? ~3u : ~0u;
         rsrc = make_rsrc(s, mode == 0 ? 4 : (rows * pitch + 3) & ~(int64_t)3);
-        const int r = (wave * 64) % ROWS;
-        dst = r * 16;
-        const int64_t grow = GU ? row0 + 64 * (wave / 2) + (wave % 2) * gu_rows : row0 + r;
-        off = (uint32_t)((grow + lane) * pitch);
+#pragma unroll
+        for (int c = 0; c < NPW; ++c) {
+            const int ch = (wave + 4 * c) < NCH ? wave + 4 * c : wave % NCH;
+            const int r = ch * 64;
+            dst[c] = r * 16;
+            const int64_t grow = GU ? row0 + 64 * (wave / 2) + (wave % 2) * gu_rows : row0 + r;
+            off[c] = (uint32_t)((grow + lane) * pitch);
+        }
     }
     __device__ __forceinline__ void issue(int64_t grp, uint32_t slot) const {
-        dma16(rsrc, (off + (uint32_t)(grp * SG) * kmul) & mask, 0u, slot + (uint32_t)dst);
+#pragma unroll
+        for (int c = 0; c < NPW; ++c)
+            dma16(rsrc, (off[c] + (uint32_t)(grp * SG) * kmul) & mask, 0u, slot + (uint32_t)dst[c]);
     }
 };
 
@@ -292,14 +303,14 @@ template <int F> __device__ __forceinline__ v8bf to_bf16(const v8i& f, int q, fl
 }
 
 // Copy instructions a wave issues at the last half (position J mod 8) of a
-// ring unit: TL tile copies, plus the 2 scale-group copies at position JS.
-constexpr int copies_at(int J, int TL, int JS) { return TL + ((J % 8 + 8) % 8 == JS ? 2 : 0); }
+// ring unit: TL tile copies, plus the NSC scale-group copies at position JS.
+constexpr int copies_at(int J, int TL, int JS, int NSC) { return TL + ((J % 8 + 8) % 8 == JS ? NSC : 0); }
 // Copies issued at the last halves of the NSL-2 units before the unit that
 // ends at position J (still allowed in flight when that half waits for the
 // next unit's copies); units are SU halves long.
-constexpr int copies_after(int J, int NSL, int SU, int TL, int JS) {
+constexpr int copies_after(int J, int NSL, int SU, int TL, int JS, int NSC) {
     int n = 0;
-    for (int d = 1; d <= NSL - 2; ++d) n += copies_at(J - d * SU, TL, JS);
+    for (int d = 1; d <= NSL - 2; ++d) n += copies_at(J - d * SU, TL, JS, NSC);
     return n;
 }
 
@@ -321,6 +332,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     static_assert(!PRECISE || (FA != E2M1 && FB != E2M1), "precise mode takes FP8 operands");
     constexpr bool GU = HF >= 0;
     static_assert(!GU || (BN == 256 && FA != E2M1 && FB != E2M1 && !PRECISE), "gate/up epilogue configuration");
+    constexpr int SM = BM / 2, SN = BN / 2;                // a wave's sub-tile (2 x 2 waves)
     using IA = OpInfo<FA>;
     using IB = OpInfo<FB>;
     // Ring unit: SU K halves.  Copies fetch RB contiguous bytes per row, and
@@ -333,10 +345,12 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     constexpr int RBA = SU * IA::kh, RBB = SU * IB::kh;  // bytes per row per unit
     constexpr int A_H = BM * RBA, B_H = BN * RBB;        // bytes of one unit of each tile
     constexpr int SLOT = A_H + B_H;
-    constexpr int SCB = 16 * (BM + BN);                    // scale bytes of a group of SG K steps
-    constexpr int FM = BM / 64, FN = BN / 64;              // 32-row fragments per wave
-    constexpr int WN = BN / 2;                             // columns of a wave's sub-tile
+    constexpr int SRA = ScaleLoader<BM>::SROWS, SRB = ScaleLoader<BN>::SROWS;
+    constexpr int SCB = 16 * (SRA + SRB);                  // scale bytes of a group of SG K steps
+    constexpr int FM = SM / 32, FN = SN / 32;              // 32-row fragments per wave
+    constexpr int WN = SN;                                 // columns of a wave's sub-tile
     constexpr int NM = FM * FN;                            // MFMAs per half
+    static_assert(SM % 32 == 0 && SN % 32 == 0, "sub-tiles of whole fragments");
     // ring slots: eight, four or two, the most that fit in LDS (a power of
     // two that divides the 8 / SU units of the unrolled group of eight halves)
     constexpr int LDS_BYTES = 160 * 1024;
@@ -368,7 +382,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     const int gq = lane >> 5;                            // K block of the instruction this lane feeds
     const int64_t pA = g.ma == 1 ? g.K / 32 : g.K / 128;  // scale pitch of the operand rows
     const int64_t pB = g.mb == 1 ? g.K / 32 : g.K / 128;
-    const int rA = wm * (BM / 2) + (lane & 31), rB = wn * (BN / 2) + (lane & 31);
+    const int rA = wm * SM + (lane & 31), rB = wn * SN + (lane & 31);
 
     // operand extents for the buffer resources (validated below 4 GiB); a
     // grouped A has M = total rows, whatever its offsets claim
@@ -387,6 +401,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     lsB.init(g.mb, t.sB, g.K, g.N, b_row0, wave, lane, g.inter);
     constexpr int TLA = TileLoader<RBA, BM, LU>::PER_WAVE;
     constexpr int TL = TLA + TileLoader<RBB, BN, LU, GU>::PER_WAVE;  // tile copies per unit
+    constexpr int NSC = ScaleLoader<BM>::NPW + ScaleLoader<BN, GU>::NPW;  // scale copies per group
 
     // Scale operand of a fragment row, from the staged dword: the byte for K
     // half h ends up at byte 2h (BLK32: blocks 2h + gq; BLK128: the step's
@@ -519,7 +534,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     auto issue_scales = [&](int64_t grp) __attribute__((always_inline)) {
         const uint32_t cs = LC0 + (uint32_t)(grp & 1) * (LC1 - LC0);  // (a select here defeats SROA)
         lsA.issue(grp, cs);
-        lsB.issue(grp, cs + 16u * BM);
+        lsB.issue(grp, cs + 16u * SRA);
     };
     // Schedule: unit v (halves SU*v ..) lives in slot v % NSL.  Its copies are
     // issued in the last half of unit v - NSL, right after that half's
@@ -528,7 +543,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     // first, with the copies of the unit holding half 8u; its issuing half
     // sits at position JS (mod 8):
     constexpr int JS = ((8 - NSL * SU + SU - 1) % 8 + 8) % 8;
-    static_assert(NSL * TL + 2 <= 63, "copies in flight must fit the vmcnt counter");
+    static_assert(NSL * TL + NSC <= 63, "copies in flight must fit the vmcnt counter");
     static_assert((8 / SU) % NSL == 0, "slots must repeat within a group of eight halves");
 
     // One half j at position J = j % 8 of a group of eight halves (four K
@@ -550,7 +565,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
         if constexpr (LAST) {
             // wait for the next unit's copies; those of the NSL-2 units
             // issued after them may still run
-            __builtin_amdgcn_s_waitcnt(wait_vm(copies_after(J, NSL, SU, TL, JS)));
+            __builtin_amdgcn_s_waitcnt(wait_vm(copies_after(J, NSL, SU, TL, JS, NSC)));
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
             dst = lds_addr(slot(std::integral_constant<int, CUR>{}));
@@ -565,7 +580,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
             for (int i = 0; i < FM; ++i) da[i] = *reinterpret_cast<const uint32_t*>(cs + (rA + 32 * i) * 16 + oa);
 #pragma unroll
             for (int jj = 0; jj < FN; ++jj)
-                db[jj] = *reinterpret_cast<const uint32_t*>(cs + 16 * BM + (rB + 32 * jj) * 16 + ob);
+                db[jj] = *reinterpret_cast<const uint32_t*>(cs + 16 * SRA + (rB + 32 * jj) * 16 + ob);
         }
         // scale operands of step (j+1)/2 from the staged dwords
         auto form_scales = [&]() __attribute__((always_inline)) {
@@ -656,7 +671,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
 #pragma unroll
     for (int jj = 0; jj < FN; ++jj) {
         fb[0][jj] = frag_b(s0, jj, 0);
-        sb[0][jj] = sreg(smB, *reinterpret_cast<const uint32_t*>(c0 + 16 * BM + (rB + 32 * jj) * 16 + dwB(0)), sshift(smB, shB, 0));
+        sb[0][jj] = sreg(smB, *reinterpret_cast<const uint32_t*>(c0 + 16 * SRA + (rB + 32 * jj) * 16 + dwB(0)), sshift(smB, shB, 0));
     }
     if constexpr (PRECISE) {
 #pragma unroll
@@ -682,9 +697,9 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     float alpha = 1.0f;
     if (g.ma == 0) alpha *= ((const float*)g.sA)[0];
     if (g.mb == 0) alpha *= ((const float*)g.sB)[0];
-    const int64_t row_base = t.m0 + wm * (BM / 2), col_base = t.n0 + wn * WN;
+    const int64_t row_base = t.m0 + wm * SM, col_base = t.n0 + wn * WN;
     // rows and columns of this wave's sub-tile that exist in C
-    const int mlim = (int)min(t.m_end - row_base, (int64_t)(BM / 2));
+    const int mlim = (int)min(t.m_end - row_base, (int64_t)SM);
     const int nlim = (int)min(g.N - col_base, (int64_t)WN);
     // staging room per wave: a slot each, or half of slot 0 / 1 with two slots
     constexpr int CAP = NSL >= 4 ? SLOT : SLOT / 2;

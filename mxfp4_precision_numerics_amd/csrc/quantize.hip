@@ -315,8 +315,10 @@ __global__ void __launch_bounds__(256) k_pt_cast(const void* __restrict__ x, int
                     uint8_t* const dst = q_col + (tc + 8 * cg) * rows + tr + 8 * g;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        st_nt8(dst + j * rows, make_uint2(lo[j], lo[4 + j]));
-                        st_nt8(dst + (4 + j) * rows, make_uint2(hi[j], hi[4 + j]));
+                        // plain stores for the transposed output (its 128-byte
+                        // segments of neighbouring tiles meet in L2)
+                        *reinterpret_cast<uint2*>(dst + j * rows) = make_uint2(lo[j], lo[4 + j]);
+                        *reinterpret_cast<uint2*>(dst + (4 + j) * rows) = make_uint2(hi[j], hi[4 + j]);
                     }
                 }
             }
@@ -535,7 +537,107 @@ __global__ void __launch_bounds__(256) k_mx_dual(const void* __restrict__ x, int
     if (live) {
         uint8_t* const dst = q_col + (tc + 8 * cg) * rows + tr + 8 * g;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) st_nt8(dst + j * rows, make_uint2(lo[j], hi[j]));
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint2*>(dst + j * rows) = make_uint2(lo[j], hi[j]);
+    }
+}
+
+// bf16 input: the same tile phases on the raw bf16 pairs.  Codes come from
+// the packed bf16 converter (clamped on the 16-bit patterns), so a lane holds
+// its 8 row-phase vectors as loaded (4 registers each) and the column phase
+// builds each converter operand (two rows of one column) with one byte
+// permute: fewer registers than the binary32 form, so more tiles per CU.
+template <int F>
+__device__ __forceinline__ uint2 mx_codes_bf16x8(const uint32_t (&w)[4], uint32_t amax16, uint8_t& sbyte) {
+    const bool bad = amax16 >= 0x7F80u;
+    const int e = block_exp<F>(amax16 >> 7);
+    const float sc = exp2i(e);
+    const uint32_t lim = (uint32_t)(e + 127 + FmtInfo<F>::emax) << 7 | FmtInfo<F>::max_mant_bf16;
+    const uint32_t lim2 = lim | (lim << 16);
+    uint32_t c0 = cvt2_bf16_fp8<F>(0u, clamp2_bf16(w[0], lim2), sc, false);
+    c0 = cvt2_bf16_fp8<F>(c0, clamp2_bf16(w[1], lim2), sc, true);
+    uint32_t c1 = cvt2_bf16_fp8<F>(0u, clamp2_bf16(w[2], lim2), sc, false);
+    c1 = cvt2_bf16_fp8<F>(c1, clamp2_bf16(w[3], lim2), sc, true);
+    if (bad) { c0 = 0x7F7F7F7Fu; c1 = 0x7F7F7F7Fu; }
+    sbyte = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
+    return make_uint2(c0, c1);
+}
+
+template <int F>
+__global__ void __launch_bounds__(256) k_mx_dual_bf16(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                      int64_t ld, uint8_t* __restrict__ q_row,
+                                                      uint8_t* __restrict__ s_row, uint8_t* __restrict__ q_col,
+                                                      uint8_t* __restrict__ s_col) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[TT * TT * 2];
+    const int64_t tr = (int64_t)blockIdx.y * TT, tc = (int64_t)blockIdx.x * TT;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int ch = lane & 15;
+    const bool cok = tc + 8 * ch < cols;  // rows % 32 == 0, cols % 32 == 0
+    auto lds_chunk = [&](int r, int c) __attribute__((always_inline)) -> uint8_t* {
+        return tile + (r * TT + 8 * chunk_swz(r, c)) * 2;
+    };
+    {
+        uint32_t raw[8][4];
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int r = 16 * it + 4 * w + (lane >> 4);
+            uint32_t u[8];
+            load_raw8<1>(x, (tr + r) * ld + tc + 8 * ch, cok && tr + r < rows, u);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) raw[it][k] = u[k];
+        }
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int r = 16 * it + 4 * w + (lane >> 4);
+            if (q_row) {
+                const uint32_t m2 = pk_max_u16(pk_max_u16(raw[it][0] & 0x7FFF7FFFu, raw[it][1] & 0x7FFF7FFFu),
+                                               pk_max_u16(raw[it][2] & 0x7FFF7FFFu, raw[it][3] & 0x7FFF7FFFu));
+                const uint32_t a = m2 & 0xFFFFu, b = m2 >> 16;
+                const uint32_t m = quad_max_u32(a > b ? a : b);  // the 4 lanes of a 32-column block
+                uint8_t sb;
+                const uint2 c = mx_codes_bf16x8<F>(raw[it], m, sb);
+                if (cok && tr + r < rows) {
+                    st_nt8(q_row + (tr + r) * cols + tc + 8 * ch, c);
+                    if ((lane & 3) == 0) s_row[(tr + r) * (cols / 32) + (tc + 8 * ch) / 32] = sb;
+                }
+            }
+            *reinterpret_cast<uint4*>(lds_chunk(r, ch)) = make_uint4(raw[it][0], raw[it][1], raw[it][2], raw[it][3]);
+        }
+    }
+    __syncthreads();
+    // column phase: patch rows 8g .. 8g+7, columns 8cg .. 8cg+7 of the tile;
+    // word k of a patch row holds columns 2k (low half) and 2k+1
+    const int g = lane >> 2, cg = 4 * w + (lane & 3);
+    uint32_t wv[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(lds_chunk(8 * g + i, cg));
+        wv[i][0] = v.x; wv[i][1] = v.y; wv[i][2] = v.z; wv[i][3] = v.w;
+    }
+    const bool live = tr + 8 * g < rows && tc + 8 * cg < cols;  // uniform over the 4 lanes of a column block
+    uint8_t* const dst = q_col + (tc + 8 * cg) * rows + tr + 8 * g;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = pk_max_u16(m, wv[i][k] & 0x7FFF7FFFu);
+        m = quad4_max_pk16(m);  // lanes l, l^4, l^8, l^12: the 32 rows of the column block
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // rows 2p, 2p+1 of column 2k + h as one bf16 pair
+            const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+            uint32_t pr[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) pr[p] = __builtin_amdgcn_perm(wv[2 * p + 1][k], wv[2 * p][k], sel);
+            uint8_t sb;
+            const uint2 c = mx_codes_bf16x8<F>(pr, h ? m >> 16 : m & 0xFFFFu, sb);
+            const int j = 2 * k + h;
+            if (live) {
+                // plain store: the 128-byte column segments of neighbouring
+                // tiles meet in L2 (measured 9% faster than streaming stores)
+                *reinterpret_cast<uint2*>(dst + j * rows) = c;
+                if ((g & 3) == 0) s_col[(tc + 8 * cg + j) * (rows / 32) + (tr + 8 * g) / 32] = sb;
+            }
+        }
     }
 }
 
@@ -672,7 +774,10 @@ template <int F, int SRC>
 static void launch_mx_dual_t(const void* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* q_row, uint8_t* s_row,
                              uint8_t* q_col, uint8_t* s_col, hipStream_t st) {
     const dim3 grid((unsigned)((cols + TT - 1) / TT), (unsigned)((rows + TT - 1) / TT));
-    hipLaunchKernelGGL((k_mx_dual<F, SRC>), grid, dim3(256), 0, st, x, rows, cols, ld, q_row, s_row, q_col, s_col);
+    if constexpr (SRC == 1)
+        hipLaunchKernelGGL((k_mx_dual_bf16<F>), grid, dim3(256), 0, st, x, rows, cols, ld, q_row, s_row, q_col, s_col);
+    else
+        hipLaunchKernelGGL((k_mx_dual<F, SRC>), grid, dim3(256), 0, st, x, rows, cols, ld, q_row, s_row, q_col, s_col);
 }
 
 hipError_t launch_quantize_mx(const void* x, int src, int64_t rows, int64_t cols, int64_t ld, int fmt, uint8_t* q_row,

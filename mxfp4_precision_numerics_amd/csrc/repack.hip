@@ -244,7 +244,7 @@ __global__ void __launch_bounds__(256) k_fp4_row_to_fp8_col(const uint8_t* __res
                 hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
                 if (bad) { lo = 0x7F7F7F7Fu; hi = 0x7F7F7F7Fu; }
                 if (live) {
-                    st_nt8(q8 + (c0 + j) * rows + tr + 8 * g, make_uint2(lo, hi));
+                    *reinterpret_cast<uint2*>(q8 + (c0 + j) * rows + tr + 8 * g) = make_uint2(lo, hi);
                     if ((g & 3) == 0) s8[(c0 + j) * (rows / 32) + (tr + 8 * g) / 32] = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
                 }
             }
