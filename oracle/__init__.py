@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "liboracle.so")
+# MXQ_ORACLE_LIB selects another build of oracle.c (the sanitizer build of
+# the CPU hygiene tests); the default is the optimized one.
+_LIB_PATH = os.environ.get("MXQ_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 E4M3, E5M2, E2M1 = 0, 1, 2
 SRC_F32, SRC_BF16, SRC_F64 = 0, 1, 2  # float64 input: MX quantizer only

@@ -17,13 +17,23 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off"
           "-fno-fast-math", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 
 
-def build(verbose: bool = False) -> str:
-    cmd = ["gcc", *CFLAGS, SRC, "-o", LIB + ".tmp", "-lm"]
+# The same library under AddressSanitizer and UndefinedBehaviorSanitizer (CPU
+# checks of the oracle itself: out-of-bounds, overflow, misaligned access).
+# Loaded into an uninstrumented Python with gcc's ASan runtime preloaded.
+SAN_LIB = os.path.join(HERE, "liboracle_san.so")
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    out = SAN_LIB if sanitize else LIB
+    flags = [f for f in CFLAGS if not (sanitize and f == "-O2")] + (SAN_FLAGS if sanitize else [])
+    cmd = ["gcc", *flags, SRC, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
