@@ -268,6 +268,8 @@ def rows_c2(ctx, rows):
     if ctx.want("c2_mx_w"):
         rows["c2_mx_w"] = ctx.bw("a4 MX E4M3 row quantize, W 14336x4096 bf16", N * K * (2 + 1 + 1 / 32),
                                  ctx.timed(lambda: mxq.quantize_mx(w, mxq.E4M3, qw, sw)))
+    if not (ctx.want("c2_gemm_precise") or ctx.want("c2_gemm_native")):
+        return
     mxq.quantize_mx(x, mxq.E4M3, qx, sx)
     mxq.quantize_mx(w, mxq.E4M3, qw, sw)
     C = ctx.f32(M, N)
