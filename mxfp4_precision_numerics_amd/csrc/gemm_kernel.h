@@ -177,8 +177,9 @@ __device__ __forceinline__ void dma16(const v4u& rsrc, uint32_t voff, uint32_t s
 // (w + 4i) * RP ...); lane L's position holds the global chunk that belongs
 // there under the lds_off() swizzle, which is the same for every piece.
 // Rows past the operand's end (a partial last tile) fall outside the
-// buffer's range and read zero; in a grouped operand they read the next
-// group's rows.  Either way they only feed outputs that are never stored.
+// buffer's range and read zero; A's range ends at the end of the tile's
+// group, so rows past a group read zero too, without memory traffic.
+// Either way they only feed outputs that are never stored.
 // The per-lane offset of piece 0 is kept; piece i adds i * RP * 4 rows.  The
 // unit enters as the uniform offset (operands stay below 4 GiB), except with
 // LANE_UNIT: the buffer's range check covers the per-lane offset only, and a
@@ -383,9 +384,13 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     const int64_t pA = g.ma == 1 ? g.K / 32 : g.K / 128;  // scale pitch of the operand rows
     const int64_t pB = g.mb == 1 ? g.K / 32 : g.K / 128;
     const int rA = wm * SM + (lane & 31), rB = wn * SN + (lane & 31);
+    // FP8 / FP4 MFMA: fragments of rows that all lie past the tile's last row
+    // (a group's partial tile, the last m-tile) are neither read nor multiplied
+    const int fact = __builtin_amdgcn_readfirstlane(
+        (int)max(min((t.m_end - (t.m0 + wm * SM) + 31) / 32, (int64_t)FM), (int64_t)0));
 
-    // operand extents for the buffer resources (validated below 4 GiB); a
-    // grouped A has M = total rows, whatever its offsets claim
+    // operand extents for the buffer resources (validated below 4 GiB): A's
+    // ends with the tile's rows (the group's end), B's with the operand
     // FP4 x FP4 units are two K steps: the last one may run past a row's end
     constexpr bool LU = SU > 2;
     TileLoader<RBA, BM, LU> ldA;
@@ -393,11 +398,11 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     // gate/up tiles: tile n0 (a multiple of 256) covers intermediate columns
     // n0 / 2 .. + 127, gate rows from n0 / 2, up rows inter further
     const int64_t b_row0 = GU ? t.n0 / 2 : t.n0;
-    ldA.init(g.A, g.M * lda, lda, t.m0, wave, lane);
+    ldA.init(g.A, t.m_end * lda, lda, t.m0, wave, lane);
     ldB.init(t.B, g.N * ldb, ldb, b_row0, wave, lane, g.inter);
     ScaleLoader<BM> lsA;
     ScaleLoader<BN, GU> lsB;
-    lsA.init(g.ma, g.sA, g.K, g.M, t.m0, wave, lane);
+    lsA.init(g.ma, g.sA, g.K, t.m_end, t.m0, wave, lane);
     lsB.init(g.mb, t.sB, g.K, g.N, b_row0, wave, lane, g.inter);
     constexpr int TLA = TileLoader<RBA, BM, LU>::PER_WAVE;
     constexpr int TL = TLA + TileLoader<RBB, BN, LU, GU>::PER_WAVE;  // tile copies per unit
@@ -603,9 +608,10 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
             constexpr int i = k % FM, jj = k / FM;
             if constexpr (!PRECISE) {
                 static_assert(!SB, "single-buffered fragments are a precise-mode layout");
-                acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    fa[P][i], fb[P][jj], acc[i][jj], IA::code, IB::code, 2 * P, (int)sa[SP][i], 2 * P,
-                    (int)sb[SP][jj]);
+                if (i < fact)
+                    acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fa[P][i], fb[P][jj], acc[i][jj], IA::code, IB::code, 2 * P, (int)sa[SP][i], 2 * P,
+                        (int)sb[SP][jj]);
             } else {
                 // Quarter q of every fragment pair: one bf16 instruction of
                 // K = 16 on operands converted during quarter q - 1 (the
@@ -632,7 +638,9 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
             // next half's fragments, one per MFMA slot while they last (the
             // single-buffered precise tile: in its last quarter, into set 0)
             constexpr int R0 = SB ? 3 * NM : 0;
-            if constexpr (s >= R0 && s < R0 + FM) fa[SB ? 0 : Q][s - R0] = frag_a(nxt, s - R0, SUB1);
+            if constexpr (s >= R0 && s < R0 + FM) {
+                if (PRECISE || s - R0 < fact) fa[SB ? 0 : Q][s - R0] = frag_a(nxt, s - R0, SUB1);
+            }
             if constexpr (s >= R0 + FM && s < R0 + FM + FN) fb[SB ? 0 : Q][s - R0 - FM] = frag_b(nxt, s - R0 - FM, SUB1);
             // copies of unit + NSL, spread evenly over the half's MFMA slots
             // (a copy waits for the CU's address unit; bursts stall the MFMAs)
