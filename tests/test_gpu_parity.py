@@ -435,6 +435,29 @@ def test_fp4_col_specials():
     assert np.all(s8[128:160, 1] == 0xFF)
 
 
+def test_fp4_col_scale_spread_edges():
+    """Scale bytes drawn from the edges of the kernel's two conversion paths
+    (spreads of 243/244 and 252/253 binades among a lane's 8 tokens, bytes 0
+    and 254, column exponents set by other lanes' far larger scales), with
+    zero codes, zero rows and signed zeros mixed in: bit-exact."""
+    g = np.random.Generator(np.random.PCG64(21))
+    rows, cols = 256, 512
+    edges = np.array([0, 1, 2, 9, 10, 11, 120, 243, 244, 245, 251, 252, 253, 254], np.uint8)
+    s4 = edges[g.integers(0, len(edges), size=(rows, cols // 32))]
+    q4 = g.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    q4[g.random(q4.shape) < 0.3] = 0
+    q4[g.random(q4.shape) < 0.05] = 0x88
+    q4[g.integers(0, rows, 24), :] = 0
+    # 8-token groups whose scales sit at one end, next to groups at the other
+    for r0 in range(0, rows, 64):
+        s4[r0:r0 + 8] = 254
+        s4[r0 + 8:r0 + 16] = g.integers(0, 12, size=(8, cols // 32)).astype(np.uint8)
+    q8, s8 = gpu_fp4_col(q4, s4)
+    oq, os_ = O.fp4_row_to_fp8_col(q4, s4)
+    assert np.array_equal(s8, os_)
+    assert np.array_equal(q8, oq)
+
+
 def test_fp4_col_of_gpu_mx_quantize():
     """BF16 activations -> MXFP4 rows (GPU) -> FP8 columns (GPU) against the
     oracle's own chain."""
