@@ -275,12 +275,13 @@ struct ScaleLoader {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-// 2^(b-127) as a float: b = 0 is the subnormal 2^-127, b = 255 NaN.  The
-// subnormal 2^-127 scaled by 2^b is exact for b = 0 .. 254 and overflows to
-// Inf at 255; fma(x, 0, x) is x for finite x and NaN for Inf.
-__device__ __forceinline__ float e8m0_f32(uint32_t b) {
-    const float x = __builtin_ldexpf(__builtin_bit_cast(float, 0x00400000u), (int)b);
-    return __builtin_fmaf(x, 0.0f, x);
+// Byte k of d as the scale operand of the scaled converters, which read
+// only their scale's exponent field, as an E8M0 byte: the byte moved to bits
+// 23..30 (field 0 is 2^-127, field 255 NaN).
+__device__ __forceinline__ float e8m0_field(uint32_t d, int k) {
+    const int sh = 23 - 8 * k;
+    const uint32_t v = sh >= 0 ? (d << sh) : (d >> -sh);
+    return __builtin_bit_cast(float, v & 0x7F800000u);
 }
 
 // Bytes 8q .. 8q+7 of an FP8 fragment (dwords 2q, 2q+1) as 8 bf16 values
@@ -500,11 +501,11 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     // in quarter order per fragment).
     float fsa[FM], fsb[FN];
     auto conv_a = [&](int set, int h, int i, int q, int ss) __attribute__((always_inline)) -> v8bf {
-        if ((q & 1) == 0) fsa[i] = e8m0_f32((sa[ss][i] >> (8 * (2 * h + q / 2))) & 0xFFu);
+        if ((q & 1) == 0) fsa[i] = e8m0_field(sa[ss][i], 2 * h + q / 2);
         return to_bf16<FA>(fa[set][i], q, fsa[i]);
     };
     auto conv_b = [&](int set, int h, int jj, int q, int ss) __attribute__((always_inline)) -> v8bf {
-        if ((q & 1) == 0) fsb[jj] = e8m0_f32((sb[ss][jj] >> (8 * (2 * h + q / 2))) & 0xFFu);
+        if ((q & 1) == 0) fsb[jj] = e8m0_field(sb[ss][jj], 2 * h + q / 2);
         return to_bf16<FB>(fb[set][jj], q, fsb[jj]);
     };
 
