@@ -18,7 +18,9 @@
  *    All work is enqueued asynchronously on it.
  *  - Every call validates its arguments on the host BEFORE touching HIP and
  *    returns an mxq_status.  Device faults surface at the caller's next
- *    synchronisation.  A zero-size problem returns MXQ_OK with no launch.
+ *    synchronisation.  A zero-size problem (no rows, or no columns) returns
+ *    MXQ_OK with no launch once its formats and shape rules pass; its data
+ *    pointers are then not checked and may be NULL (an empty tensor's).
  *  - All tensors are row-major.  16-byte alignment is required of every
  *    tensor base pointer and of every row pitch in bytes.
  *  - The library holds no state; calls are reentrant.  Calls that write the

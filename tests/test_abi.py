@@ -66,6 +66,9 @@ def test_quantize_per_tensor_validation(L):
     assert qpt(L, ld=68) == EALIGN                     # 68 * 2 bytes is not a multiple of 16
     assert qpt(L, rows=0) == OK                        # zero-size: no launch
     assert qpt(L, cols=0, ld=0) == OK
+    # an empty tensor's NULL data pointers are accepted at zero size; the shape rules still hold
+    assert qpt(L, rows=0, x=None, amax=None, scale=None, sinv=None, q_row=None) == OK
+    assert qpt(L, rows=0, x=None, cols=60, ld=60) == ESHAPE
 
 
 def qmx(L, **kw):
@@ -84,6 +87,8 @@ def test_quantize_mx_validation(L):
     assert qmx(L, q_col=P, s_col=P, rows=48) == ESHAPE
     assert qmx(L, s_row=P + 1) == EALIGN
     assert qmx(L, rows=0) == OK
+    assert qmx(L, rows=0, x=None, q_row=None, s_row=None) == OK
+    assert qmx(L, rows=0, x=None, fmt=7) == EFMT
 
 
 def test_repack_validation(L):
@@ -93,6 +98,7 @@ def test_repack_validation(L):
     assert f(None, P, None, 4, 4, 128, P, P, None) == ENULL
     assert f(P, P, P + 2, 4, 4, 128, P, P, None) == EALIGN
     assert f(P, P, P, 4, 0, 128, P, P, None) == OK
+    assert f(None, None, None, 0, 0, 128, None, None, None) == OK
 
 
 def test_fp4_col_validation(L):
@@ -105,6 +111,7 @@ def test_fp4_col_validation(L):
     assert f(P + 8, P, 64, 64, P, P, None) == EALIGN
     assert f(P, P, 64, 64, P + 8, P, None) == EALIGN
     assert f(P, P, 0, 64, P, P, None) == OK
+    assert f(None, None, 0, 64, None, None, None) == OK
 
 
 def test_swiglu_validation(L):
@@ -120,6 +127,7 @@ def test_swiglu_validation(L):
     assert f(P, 1, 64, 64, 132, 0, P, P, None) == EALIGN     # row pitch of 264 bytes
     assert f(P, 1, 64, 64, 128, 0, P + 8, P, None) == EALIGN
     assert f(P, 1, 0, 64, 128, 0, P, P, None) == OK
+    assert f(None, 1, 0, 64, 128, 0, None, None, None) == OK
 
 
 def test_gemm_validation(L):
@@ -138,6 +146,8 @@ def test_gemm_validation(L):
     assert g(P, 0, P, 1, P, 0, P, 1, 16, 18, 128, P, 0, 18, None) == EALIGN   # ldc*4 % 16
     assert g(P + 4, 0, P, 1, P, 0, P, 1, 16, 16, 128, P, 0, 16, None) == EALIGN
     assert g(P, 0, P, 1, P, 0, P, 1, 0, 16, 128, P, 0, 16, None) == OK        # M = 0
+    assert g(None, 0, None, 1, P, 0, P, 1, 0, 16, 128, None, 0, 16, None) == OK  # M = 0, empty A and C
+    assert g(None, 0, None, 1, P, 0, P, 1, 0, 16, 100, None, 0, 16, None) == ESHAPE  # K rule at M = 0
     # operands addressed with 32-bit offsets: 2^25 rows x 128 bytes is 4 GiB
     assert g(P, 0, P, 0, P, 0, P, 0, 1 << 25, 16, 128, P, 0, 16, None) == ESHAPE
     assert g(P, 0, P, 0, P, 2, P, 0, 16, 1 << 26, 128, P, 0, 1 << 26, None) == ESHAPE  # E2M1 B: 4 GiB
@@ -145,6 +155,7 @@ def test_gemm_validation(L):
     assert gg(P, 0, P, 2, P, 0, P, 1, None, 4, 64, 128, 128, P, 1, None) == ENULL
     assert gg(P, 0, P, 2, P, 0, P, 1, P, 5000, 64, 128, 128, P, 1, None) == ESHAPE
     assert gg(P, 0, P, 2, P, 0, P, 1, P, 0, 64, 128, 128, P, 1, None) == OK   # no groups
+    assert gg(None, 0, None, 2, P, 0, P, 1, P, 4, 0, 128, 128, None, 1, None) == OK  # no rows
     assert gg(P, 0, P, 0, P, 0, P, 0, P, 4, 1 << 25, 128, 128, P, 1, None) == ESHAPE  # A 4 GiB
 
 
@@ -163,6 +174,8 @@ def test_fused_expert_up_projection_validation(L):
     assert f(P, 0, P, 1, P, 0, P, 1, P, 4, 64, 128, 256, 0, P + 8, P, None) == EALIGN
     assert f(P, 0, P, 1, P, 0, P, 1, P + 2, 4, 64, 128, 256, 0, P, P, None) == EALIGN
     assert f(P, 0, P, 1, P, 0, P, 1, P, 4, 0, 128, 256, 0, P, P, None) == OK       # no rows
+    assert f(None, 0, None, 1, P, 0, P, 1, P, 4, 0, 128, 256, 0, None, None, None) == OK  # empty A, h
+    assert f(None, 0, None, 1, P, 0, P, 1, P, 4, 0, 96, 256, 0, None, None, None) == ESHAPE
     assert f(P, 0, P, 0, P, 0, P, 0, P, 4, 1 << 25, 128, 128, 0, P, P, None) == ESHAPE  # A 4 GiB
 
 
