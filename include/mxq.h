@@ -172,7 +172,8 @@ int mxq_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const int32_t* g
  * [-127, 127] over the exact values v = E2M1(code) * 2^(s-127) (all zero:
  * e = -127); codes = saturating RNE E4M3 of v / 2^e; a NaN block gets byte
  * 0xFF and codes 0x7F.
- * Rules: rows % 32 == 0, cols % 32 == 0; q4 and q8 16-byte aligned.  The
+ * Rules: rows % 32 == 0, cols % 32 == 0; q4 and q8 16-byte aligned (s4 and
+ * s8 any alignment); at most 2^31 - 1 tiles of 128 rows x 256 columns.  The
  * call writes every byte of q8 and s8 and reads nothing else.
  */
 int mxq_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, int64_t cols, uint8_t* q8,

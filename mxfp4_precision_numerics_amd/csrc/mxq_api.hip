@@ -105,6 +105,7 @@ int mxq_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, i
     if (rows == 0 || cols == 0) return MXQ_OK;
     if (!q4 || !s4 || !q8 || !s8) return MXQ_ERR_NULL;
     if (!aligned16(q4) || !aligned16(q8)) return MXQ_ERR_ALIGN;
+    if (((rows + 127) / 128) * ((cols + 255) / 256) > MAX_GRID_X) return MXQ_ERR_SHAPE;  // one block per tile
     return hip_status(mxq::launch_fp4_row_to_fp8_col(q4, s4, rows, cols, q8, s8, as_stream(stream)));
 }
 

@@ -111,153 +111,240 @@ hipError_t launch_repack_fp4_to_fp8(const uint8_t* q4, const uint8_t* s4, const 
 // contracts over the tokens) reads FP8 blocks along the tokens.  Reading:
 // exact dequantization, then MX block-32 E4M3 along the new rows.
 //
-// A persistent block of 256 threads walks tiles of 128 source rows x 256
-// source columns with the grid's stride; the next tile's loads are in flight
-// while the current one is converted from LDS.
-//  Row phase: wave w, step it reads source row 16*it + 4*w + l/16, 16 lanes
-//  per row, 16 codes (8 bytes) per lane: whole 128-byte lines.  Codes go to
-//  LDS as they are (4 bits each); the row's 8 scale bytes too.
-//  Column phase (twice, for columns 0..127 and 128..255 of the tile): lane l
-//  of wave w takes source rows 8*(l/4) .. +7 and columns 8*(4w + l%4) .. +7,
-//  i.e. 8 output rows of 8 tokens; the 16 lanes of a column cover its 128
-//  tokens and write a whole line.  An output block (32 tokens) spans the 4
-//  lanes that differ in lane bits 2-3.
-// Each element is m * 2^(s-127) with m an E2M1 value; its exponent is that of
-// m plus s - 127, so the block exponent is an integer max and every element
-// divided by the block scale is m * 2^(s-127-e), formed with ldexp from a
-// byte table of 2|m| (exact where it can reach E4M3's range) and rounded to
-// nearest even by the converter.  The block exponent puts the largest
-// magnitude at 256 or 384, so nothing saturates.
-// LDS rows hold 32 dwords of codes; dword index bits 2-4 are XOR-ed with the
-// row's bits 3-5, which halves the column reads' bank conflicts to 2-way.
+// One block of 256 threads per tile of 128 source rows (tokens) x 256 source
+// columns.  Row phase: the tile's codes reach LDS as 16-byte chunks (whole
+// 128-byte lines per 8 lanes) and its scale bytes as a [block][row] array.
+// Column phase: lane l of wave w owns tokens 16*(l/8) .. +15 of the 8 columns
+// 8*(8w + l%8) .. +7, so every output row gets one 16-byte store per lane and
+// 8 lanes write a whole 128-byte line; a 32-token output block spans a lane
+// and its partner 8 lanes away (one DPP row rotation).
+//
+// Two conversion paths, chosen per tile (block-uniform):
+//  * converter path, when every scale byte of the tile lies in [12, 254]:
+//    gfx950's scaled FP4 converters yield each element divided by 4, exactly
+//    (m * 2^(s-129) is a normal number for these bytes).  A first pass
+//    converts to bfloat16 and takes the block's largest magnitude as an
+//    integer max of the bit patterns; its exponent gives the E8M0 byte
+//    e + 127.  A second pass converts to binary32, and the scaled binary32 ->
+//    E4M3 converter divides by 2^(e-2) and rounds to nearest even in one
+//    step.  The smallest non-zero value, 2^-118 after the division, keeps
+//    e >= -124, so 2^(e-2) is a normal binary32 and the converter's scale
+//    (its exponent field) holds it.  Converting twice keeps the live values
+//    few (66 VGPRs, seven blocks per CU).
+//  * integer path otherwise (tiny or NaN scale bytes), one column at a time
+//    from LDS: each element's floor(log2 |v|) + 129 is L(m) + s, the block
+//    exponent is an integer max, and every element is 2|m| * 2^(s - 128 - e)
+//    formed with ldexp and cast by the unscaled converter; a NaN source scale
+//    makes the whole output block NaN (codes 0x7F, scale byte 0xFF).
+// In both, the block exponent puts the largest magnitude at 256 or 384, so
+// nothing saturates, and an all-zero block gets byte 0x00.  The output scale
+// bytes gather in LDS as [column][block] and leave as one 4-byte store per
+// column (the tile's 4 blocks) where alignment allows, bytes otherwise.
+// LDS rows hold 32 dwords; the dword index is XOR-ed with 8 * ((row / 16) % 4)
+// so that the column phase's reads (rows 16 apart) spread over the banks.
 // ---------------------------------------------------------------------------
+// The codes leave through plain (cached) stores: each 16-byte store is part
+// of a 128-byte line that 8 lanes complete, and these merge in L2 better
+// than streaming stores do (measured 7% faster here).
+__device__ __forceinline__ void st_line16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+typedef float v2f __attribute__((ext_vector_type(2)));
 constexpr int FC_ROWS = 128, FC_COLS = 256;
-// Persistent blocks, each walking tiles with the grid's stride: three per CU
-// of 256, the most the kernel's register use (about 155 VGPRs, three waves
-// per SIMD) keeps resident; two per CU were 4% slower, four (with spills to
-// fit) 40% slower.
-constexpr int FC_GRID = 768;
+constexpr uint32_t FC_FAST_MIN = 12;  // smallest scale byte of the converter path
 
-__device__ __forceinline__ int fc_swz(int r, int dw) { return dw ^ (((r >> 3) & 7) << 2); }
+__device__ __forceinline__ int fc_swz(int r) { return ((r >> 4) & 3) << 3; }
+
+// Scale byte k of w as a binary32 whose exponent field holds it (the other
+// bits zero): the scale operand of the scaled converters.
+__device__ __forceinline__ float fc_scale_field(uint32_t w, int k) {
+    const int sh = 23 - 8 * k;
+    const uint32_t v = sh >= 0 ? (w << sh) : (w >> -sh);
+    return as_float(v & 0x7F800000u);
+}
+
+// Converter path, source columns 2C and 2C+1 of the lane's group (byte C of
+// each code dword).  y = element / 4 (exact).  Pass 1 takes the block's
+// largest magnitudes from bfloat16 conversions (exact too: bfloat16 has the
+// binary32 exponent range), compared as integers; pass 2 converts again to
+// binary32 and casts 4 tokens at a time, so few values are live at once.
+template <int C>
+__device__ __forceinline__ void fc_fast_pair(const uint32_t (&dd)[16], const float (&sf)[16], bool live, bool pair_lo,
+                                             uint8_t* qcol, uint8_t* sbuf, int64_t rows) {
+    uint32_t mx = 0;  // |bf16| of columns 2C (low half) and 2C+1 (high half), max over tokens
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dd[i], sf[i], C);
+        mx = pk_max_u16(mx, __builtin_bit_cast(uint32_t, b) & 0x7FFF7FFFu);
+    }
+    // the partner lane (8 lanes away, the same DPP row of 16) holds the other 16 tokens of the block
+    mx = pk_max_u16(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x128, 0xF, 0xF, false));
+    // biased exponents of max|y|: e = eb - 133 (y is a quarter of the value);
+    // the codes are y / 2^(e-2), whose exponent field is eb - 8 (>= 1 unless
+    // the block is all zero, where any scale gives the zero codes)
+    const int ebe = (int)((mx >> 7) & 0xFFu), ebo = (int)(mx >> 23);
+    const float sce = as_float((uint32_t)max(ebe - 8, 1) << 23), sco = as_float((uint32_t)max(ebo - 8, 1) << 23);
+    uint32_t oe[4], oo[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        v2f y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y[q] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(dd[4 * p + q], sf[4 * p + q], C);
+        v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, y[0][0], y[1][0], sce, false);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, y[2][0], y[3][0], sce, true);
+        oe[p] = __builtin_bit_cast(uint32_t, r);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, y[0][1], y[1][1], sco, false);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, y[2][1], y[3][1], sco, true);
+        oo[p] = __builtin_bit_cast(uint32_t, r);
+    }
+    if (live) {
+        st_line16(qcol + (2 * C) * rows, make_uint4(oe[0], oe[1], oe[2], oe[3]));
+        st_line16(qcol + (2 * C + 1) * rows, make_uint4(oo[0], oo[1], oo[2], oo[3]));
+    }
+    if (pair_lo) {
+        sbuf[(2 * C) * 4] = (uint8_t)max(ebe - 6, 0);
+        sbuf[(2 * C + 1) * 4] = (uint8_t)max(ebo - 6, 0);
+    }
+}
+
+// Integer path (any scale bytes), one source column at a time; the codes are
+// read from LDS again for each column, so that this rare path holds few
+// registers.
+__device__ __forceinline__ void fc_exact(const uint32_t* codes, int tg, int cg, const uint4 sv, bool live,
+                                         bool pair_lo, uint8_t* qcol, uint8_t* sbuf, int64_t rows) {
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll 1
+    for (int j = 0; j < 8; ++j) {
+        auto code = [&](int i) __attribute__((always_inline)) {
+            const int r = 16 * tg + i;
+            return codes[r * 32 + (cg ^ fc_swz(r))] >> (4 * j);
+        };
+        int em = 0;
+        uint32_t bad = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int k = (int)code(i) & 7;
+            const int s = (int)(sw[i >> 2] >> (8 * (i & 3))) & 0xFF;
+            const int l = k < 2 ? k : (k >> 1) + 1;  // floor(log2 2|m|) + 1, 0 for a zero
+            em = max(em, k ? l + s : 0);
+            bad |= s == 0xFF;
+        }
+        em = max(em, __builtin_amdgcn_update_dpp(0, em, 0x128, 0xF, 0xF, false));
+        bad |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bad, 0x128, 0xF, 0xF, false);
+        // floor(log2 amax) - 8 (E4M3 emax), clamped below at -127 (also the
+        // all-zero block); it never exceeds 121
+        const int e = max(em - 137, -127);
+        uint32_t o[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            float y[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = 4 * p + q;
+                const uint32_t n = code(i);
+                const int k = (int)n & 7;
+                const int s = (int)(sw[i >> 2] >> (8 * (i & 3))) & 0xFF;
+                const int two_m = k < 2 ? k : (2 + (k & 1)) << ((k >> 1) - 1);
+                // |v| / 2^e = 2|m| * 2^(s - 128 - e): exact wherever it can reach
+                // E4M3's range, and at most 384
+                const float v = __builtin_amdgcn_ldexpf((float)two_m, s - 128 - e);
+                y[q] = as_float(as_uint(v) | ((n & 8u) << 28));
+            }
+            uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)r, true);
+            o[p] = bad ? 0x7F7F7F7Fu : r;
+        }
+        if (live) st_line16(qcol + j * rows, make_uint4(o[0], o[1], o[2], o[3]));
+        if (pair_lo) sbuf[j * 4] = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
+    }
+}
 
 __global__ void __launch_bounds__(256) k_fp4_row_to_fp8_col(const uint8_t* __restrict__ q4,
                                                             const uint8_t* __restrict__ s4, int64_t rows,
-                                                            int64_t cols, int64_t ntc, int64_t ntiles,
-                                                            uint8_t* __restrict__ q8, uint8_t* __restrict__ s8) {
+                                                            int64_t cols, int64_t ntc, uint8_t* __restrict__ q8,
+                                                            uint8_t* __restrict__ s8) {
     __shared__ __attribute__((aligned(16))) uint32_t codes[FC_ROWS * 32];
-    __shared__ uint8_t scales[FC_ROWS * 8];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int ch = lane & 15;
-    // the row phase's loads of tile t (zeros outside the tensor)
-    uint2 c[8];
-    uint32_t sb[8];
-    auto load_tile = [&](int64_t t) __attribute__((always_inline)) {
-        const int64_t tr = (t / ntc) * FC_ROWS, tc = (t % ntc) * FC_COLS;
+    __shared__ __attribute__((aligned(16))) uint8_t scales[8 * FC_ROWS];  // [block][row]
+    __shared__ __attribute__((aligned(16))) uint8_t sout[FC_COLS * 4];    // output scale bytes [column][block]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t tr = ((int64_t)blockIdx.x / ntc) * FC_ROWS, tc = ((int64_t)blockIdx.x % ntc) * FC_COLS;
+    // row phase: codes (zeros outside the tensor)
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int r = 16 * it + 4 * w + (lane >> 4);
-            const bool rok = tr + r < rows;
-            c[it] = make_uint2(0u, 0u);
-            sb[it] = 0;
-            if (rok && tc + 16 * ch < cols) c[it] = ld_nt8(q4 + (tr + r) * (cols / 2) + tc / 2 + 8 * ch);
-            if (rok && ch < 8 && tc + 32 * ch < cols) sb[it] = s4[(tr + r) * (cols / 32) + tc / 32 + ch];
-        }
-    };
-    int64_t t = blockIdx.x;
-    if (t < ntiles) load_tile(t);
-    for (; t < ntiles; t += gridDim.x) {
-        const int64_t tr = (t / ntc) * FC_ROWS, tc = (t % ntc) * FC_COLS;
+    for (int it = 0; it < 4; ++it) {
+        const int id = it * 256 + tid, r = id >> 3, q = id & 7;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (tr + r < rows && tc + 32 * q < cols) v = ld_nt16(q4 + (tr + r) * (cols / 2) + tc / 2 + 16 * q);
+        *reinterpret_cast<uint4*>(&codes[r * 32 + ((4 * q) ^ fc_swz(r))]) = v;
+    }
+    // scales: thread -> row tid/2, blocks 4*(tid&1) .. +3; outside the tensor
+    // the byte 127 stands in (its codes are zero, so it changes nothing)
+    bool exact = false;
+    {
+        const int r = tid >> 1, b0 = 4 * (tid & 1);
+        uint32_t sw = 0x7F7F7F7Fu;
+        if (tr + r < rows) {
+            const uint8_t* p = s4 + (tr + r) * (cols / 32) + tc / 32 + b0;
+            if ((cols & 127) == 0 && (reinterpret_cast<uintptr_t>(s4) & 3) == 0) {
+                // 4-byte aligned, and the 4 blocks are all inside or all outside
+                if (tc + 32 * b0 < cols) sw = ld_nt4(p);
+            } else {
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int r = 16 * it + 4 * w + (lane >> 4);
-            *reinterpret_cast<uint2*>(&codes[r * 32 + fc_swz(r, 2 * ch)]) = c[it];
-            if (ch < 8) scales[r * 8 + ch] = (uint8_t)sb[it];
-        }
-        __syncthreads();
-        // the next tile's loads are in flight during this tile's column phase
-        if (t + gridDim.x < ntiles) load_tile(t + gridDim.x);
-        const int g = lane >> 2;
-        // byte tables indexed by an E2M1 magnitude code k (0..7), entries 0..3 in
-        // the low word: 2|m| (0, 1, 2, 3, 4, 6, 8, 12) and floor(log2 2|m|) + 1
-        // (0 for zero)
-        constexpr uint32_t V_LO = 0x03020100u, V_HI = 0x0C080604u;
-        constexpr uint32_t L_LO = 0x02020100u, L_HI = 0x04040303u;
-#pragma unroll 1
-        for (int h = 0; h < 2; ++h) {
-            const int cg = 16 * h + 4 * w + (lane & 3);  // 8-column group of the tile, 0..31
-            // Per source row i (one token): 2|m| of columns 0,2,4,6 (vl) and
-            // 1,3,5,7 (vh) as bytes, their sign bits (bit 3 of each byte), and
-            // s - 128.  An element's floor(log2 |v|) + 129 is L(k) + s for k != 0,
-            // so the block exponent per column is a max over rows of L + s,
-            // kept on 16-bit lanes: m0 = columns (0, 4), m1 = (2, 6), m2 = (1, 5),
-            // m3 = (3, 7); 0 means no non-zero element.
-            uint32_t vl[8], vh[8], sl[8], sh[8];
-            int a[8];
-            uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
-            bool bad = false;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int r = 8 * g + i;
-                const uint32_t dd = codes[r * 32 + fc_swz(r, cg)];
-                const uint32_t sc = scales[r * 8 + (cg >> 2)];
-                bad |= sc == 0xFFu;
-                const uint32_t klo = dd & 0x07070707u, khi = (dd >> 4) & 0x07070707u;
-                sl[i] = dd & 0x08080808u;
-                sh[i] = (dd >> 4) & 0x08080808u;
-                vl[i] = __builtin_amdgcn_perm(V_HI, V_LO, klo);
-                vh[i] = __builtin_amdgcn_perm(V_HI, V_LO, khi);
-                const uint32_t ll = __builtin_amdgcn_perm(L_HI, L_LO, klo), lh = __builtin_amdgcn_perm(L_HI, L_LO, khi);
-                const uint32_t s2 = sc * 0x00010001u;
-                m0 = pk_max_u16(m0, pk_lsum_u16(ll & 0x00FF00FFu, s2));
-                m1 = pk_max_u16(m1, pk_lsum_u16((ll >> 8) & 0x00FF00FFu, s2));
-                m2 = pk_max_u16(m2, pk_lsum_u16(lh & 0x00FF00FFu, s2));
-                m3 = pk_max_u16(m3, pk_lsum_u16((lh >> 8) & 0x00FF00FFu, s2));
-                a[i] = (int)sc - 128;
-            }
-            bad = quad4_max_pk16(bad ? 1u : 0u) != 0u;  // the block's 32 tokens
-            m0 = quad4_max_pk16(m0);
-            m1 = quad4_max_pk16(m1);
-            m2 = quad4_max_pk16(m2);
-            m3 = quad4_max_pk16(m3);
-            const uint32_t em[8] = {m0 & 0xFFFFu, m2 & 0xFFFFu, m1 & 0xFFFFu, m3 & 0xFFFFu,
-                                    m0 >> 16,     m2 >> 16,     m1 >> 16,     m3 >> 16};
-            const int64_t c0 = tc + 8 * cg;
-            const bool live = tr + 8 * g < rows && c0 < cols;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                // floor(log2 amax) - 8 (E4M3 emax), clamped below at -127 (also
-                // the all-zero block); it never exceeds 121
-                const int e = max((int)em[j] - 137, -127);
-                const int b = j >> 1;  // byte of column j in vl / vh
-                float y[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t vb = (j & 1) ? vh[i] : vl[i], sb = (j & 1) ? sh[i] : sl[i];
-                    // |v| / 2^e = 2|m| * 2^(s - 128 - e), exact wherever it can
-                    // reach E4M3's range and at most 384 (no saturation)
-                    const float v = __builtin_amdgcn_ldexpf((float)((vb >> (8 * b)) & 0xFFu), a[i] - e);
-                    y[i] = as_float(as_uint(v) | ((sb << (28 - 8 * b)) & 0x80000000u));
-                }
-                uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-                lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
-                uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-                hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
-                if (bad) { lo = 0x7F7F7F7Fu; hi = 0x7F7F7F7Fu; }
-                if (live) {
-                    *reinterpret_cast<uint2*>(q8 + (c0 + j) * rows + tr + 8 * g) = make_uint2(lo, hi);
-                    if ((g & 3) == 0) s8[(c0 + j) * (rows / 32) + (tr + 8 * g) / 32] = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
-                }
+                for (int k = 0; k < 4; ++k)
+                    if (tc + 32 * (b0 + k) < cols) sw = (sw & ~(0xFFu << (8 * k))) | ((uint32_t)p[k] << (8 * k));
             }
         }
-        __syncthreads();  // LDS is free for the next tile
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t b = (sw >> (8 * k)) & 0xFFu;
+            exact |= b < FC_FAST_MIN || b == 0xFFu;
+            scales[(b0 + k) * FC_ROWS + r] = (uint8_t)b;
+        }
+    }
+    exact = __syncthreads_or(exact);
+    // column phase
+    const int tg = lane >> 3, cg = 8 * w + (lane & 7);
+    const int64_t c0 = tc + 8 * cg, r0 = tr + 16 * tg;
+    const bool live = r0 < rows && c0 < cols, pair_lo = (tg & 1) == 0;
+    const uint4 sv = *reinterpret_cast<const uint4*>(&scales[(cg >> 2) * FC_ROWS + 16 * tg]);
+    uint8_t* const qcol = q8 + c0 * rows + r0;          // output row c0 + j starts at + j * rows
+    uint8_t* const sbuf = sout + 8 * cg * 4 + (tg >> 1);  // column 8 cg + j at + 4 j
+    if (!exact) {
+        uint32_t dd[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * tg + i;
+            dd[i] = codes[r * 32 + (cg ^ fc_swz(r))];
+        }
+        // 2^(s - 129) per token: exponent field s - 2 (no byte borrows: s >= 12)
+        const uint32_t sm[4] = {sv.x - 0x02020202u, sv.y - 0x02020202u, sv.z - 0x02020202u, sv.w - 0x02020202u};
+        float sf[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sf[i] = fc_scale_field(sm[i >> 2], i & 3);
+        fc_fast_pair<0>(dd, sf, live, pair_lo, qcol, sbuf, rows);
+        fc_fast_pair<1>(dd, sf, live, pair_lo, qcol, sbuf, rows);
+        fc_fast_pair<2>(dd, sf, live, pair_lo, qcol, sbuf, rows);
+        fc_fast_pair<3>(dd, sf, live, pair_lo, qcol, sbuf, rows);
+    } else {
+        fc_exact(codes, tg, cg, sv, live, pair_lo, qcol, sbuf, rows);
+    }
+    // output scale bytes: thread -> column tc + tid, the tile's (up to) 4 blocks
+    __syncthreads();
+    const int64_t col = tc + tid;
+    if (col < cols) {
+        const int nb = (int)min((rows - tr) / 32, (int64_t)4);
+        uint8_t* const dst = s8 + col * (rows / 32) + tr / 32;
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(&sout[4 * tid]);
+        if (nb == 4 && ((rows / 32) & 3) == 0 && (reinterpret_cast<uintptr_t>(s8) & 3) == 0) {
+            *reinterpret_cast<uint32_t*>(dst) = v;
+        } else {
+            for (int b = 0; b < nb; ++b) dst[b] = (uint8_t)(v >> (8 * b));
+        }
     }
 }
 
 hipError_t launch_fp4_row_to_fp8_col(const uint8_t* q4, const uint8_t* s4, int64_t rows, int64_t cols, uint8_t* q8,
                                      uint8_t* s8, hipStream_t st) {
     const int64_t ntc = (cols + FC_COLS - 1) / FC_COLS, ntiles = ntc * ((rows + FC_ROWS - 1) / FC_ROWS);
-    const unsigned grid = (unsigned)(ntiles < FC_GRID ? ntiles : FC_GRID);
-    hipLaunchKernelGGL(k_fp4_row_to_fp8_col, dim3(grid), dim3(256), 0, st, q4, s4, rows, cols, ntc, ntiles, q8, s8);
+    hipLaunchKernelGGL(k_fp4_row_to_fp8_col, dim3((unsigned)ntiles), dim3(256), 0, st, q4, s4, rows, cols, ntc, q8,
+                       s8);
     return hipGetLastError();
 }
 

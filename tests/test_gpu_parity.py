@@ -403,10 +403,10 @@ def test_fp4_col_random(shape, srange):
     assert np.array_equal(q8, oq)
 
 
-def test_fp4_col_persistent_tiles():
-    """5216 x 8224: 1353 tiles of 128 x 256 for a persistent grid of 768
-    blocks (most take two), ragged in both directions, scales over the
-    whole byte range."""
+def test_fp4_col_many_ragged_tiles():
+    """5216 x 8224: 1353 tiles of 128 x 256, ragged in both directions,
+    mostly mid-range scales with bytes over the whole range sprinkled in (so
+    both conversion paths run, tile by tile)."""
     g = np.random.Generator(np.random.PCG64(20))
     rows, cols = 5216, 8224
     q4 = g.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
@@ -436,10 +436,10 @@ def test_fp4_col_specials():
 
 
 def test_fp4_col_scale_spread_edges():
-    """Scale bytes drawn from the edges of the kernel's two conversion paths
-    (spreads of 243/244 and 252/253 binades among a lane's 8 tokens, bytes 0
-    and 254, column exponents set by other lanes' far larger scales), with
-    zero codes, zero rows and signed zeros mixed in: bit-exact."""
+    """Scale bytes at the ends of the byte range and at spreads of 243-253
+    binades within a 32-token block (bytes 0 and 254; column exponents set by
+    other tokens' far larger scales), with zero codes, zero rows and signed
+    zeros mixed in: bit-exact."""
     g = np.random.Generator(np.random.PCG64(21))
     rows, cols = 256, 512
     edges = np.array([0, 1, 2, 9, 10, 11, 120, 243, 244, 245, 251, 252, 253, 254], np.uint8)
@@ -456,6 +456,47 @@ def test_fp4_col_scale_spread_edges():
     oq, os_ = O.fp4_row_to_fp8_col(q4, s4)
     assert np.array_equal(s8, os_)
     assert np.array_equal(q8, oq)
+
+
+def test_fp4_col_conversion_path_edges():
+    """Tiles of 128 tokens x 256 columns on either side of the converter
+    path's condition (every scale byte of the tile in [12, 254]): bytes 12 and
+    254 inside one 32-token block, a single 11, a single NaN byte, next to
+    tiles that convert on the fast path; bit-exact in every tile."""
+    g = np.random.Generator(np.random.PCG64(22))
+    rows, cols = 384, 768
+    q4 = g.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    s4 = g.integers(12, 255, size=(rows, cols // 32), dtype=np.uint8)
+    s4[0:16, 0:8] = 12                     # tile (0, 0): both edges of the range in one block
+    s4[16:32, 0:8] = 254
+    s4[5, 3] = 12
+    s4[200, 9] = 11                        # tile (1, 1): one byte below the range
+    s4[300, 17] = 0xFF                     # tile (2, 2): a NaN block
+    s4[128:256, 16:24] = 12                # tile (1, 2): all at the lower edge
+    q4[140:150, 64:96] = 0x11              # of it, smallest non-zero codes
+    q8, s8 = gpu_fp4_col(q4, s4)
+    oq, os_ = O.fp4_row_to_fp8_col(q4, s4)
+    assert np.array_equal(s8, os_)
+    assert np.array_equal(q8, oq)
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (96, 256)])
+def test_fp4_col_unaligned_scale_output(shape):
+    """The output scale array at an odd byte address (its 4-byte stores
+    fall back to bytes): bit-exact, and the bytes around it untouched."""
+    rows, cols = shape
+    g = np.random.Generator(np.random.PCG64([23, rows]))
+    q4 = g.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    s4 = g.integers(110, 140, size=(rows, cols // 32), dtype=np.uint8)
+    n = cols * (rows // 32)
+    buf = torch.full((n + 2,), 0xA5, dtype=torch.uint8, device="cuda")
+    q8 = empty_u8(cols, rows)
+    mxq.fp4_row_to_fp8_col(dev_u8(q4), dev_u8(s4), q8, buf[1:n + 1].view(cols, rows // 32))
+    b = host(buf)
+    oq, os_ = O.fp4_row_to_fp8_col(q4, s4)
+    assert b[0] == 0xA5 and b[-1] == 0xA5
+    assert np.array_equal(b[1:n + 1].reshape(cols, rows // 32), os_)
+    assert np.array_equal(host(q8), oq)
 
 
 def test_fp4_col_of_gpu_mx_quantize():
