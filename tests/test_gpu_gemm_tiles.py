@@ -12,6 +12,10 @@ workloads, at sizes where the oracle checks sampled entries in seconds.
    same instruction sequence whatever the tile.
  * Grouped GEMM with MXFP4 operands at K = 7168 (the expert GEMM's depth),
    for both the 256-row and the 128-row tile choices.
+ * Grouped GEMM on the 320 x 192 tiles (groups averaging 225-320 rows, one
+   tile per group up to 320 rows, two above): every group's rows equal, bit
+   for bit, a dense call on that group alone (other tile shapes, the same
+   per-element instruction sequence), and sampled entries meet the oracle.
 
 Tolerances: the precise mode and FP4 x FP4 (whose products fit the FP8
 MFMA's alignment window) are held to 1e-5 (REL_TOL); FP8 operands through the
@@ -166,3 +170,47 @@ def test_grouped_gemm_mxfp4_k7168(sizes):
     c, cabs = O.grouped_gemm_entries(A, 2, sA, 1, B, 2, sB, 1, off, N, K, m, n)
     r = check_gemm(Ch[m, n].astype(np.float64), c, cabs, "grouped MXFP4 K=7168")
     log(f"grouped MXFP4 K=7168 sizes {sizes}: ratio {r:.3f}")
+
+
+@pytest.mark.parametrize("fa,fb,ma,mb,out", [(0, 0, 1, 1, 0), (1, 0, 2, 1, 0), (0, 1, 1, 2, 1), (2, 2, 1, 1, 0)])
+def test_grouped_gemm_320x192_tiles(fa, fb, ma, mb, out):
+    """Groups of 300, 0, 250, 331, 229 and 280 rows (average 232: 320 x 192
+    tiles; the 331-row group takes a 320-row and an 11-row tile), N = 504 (the
+    last n-tile holds 120 columns), K = 4224 (33 K steps through a two-slot
+    ring; the tile serves K >= 4096), fp32 or bf16 output."""
+    sizes = [300, 0, 250, 331, 229, 280]
+    g = np.random.Generator(np.random.PCG64([2300, fa, fb, ma, mb, out]))
+    G, N, K = len(sizes), 504, 4224
+    off = np.zeros(G + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    R = int(off[-1])
+    A, sA = rand_operand(g, fa, ma, R, K)
+    Bs = [rand_operand(g, fb, mb, N, K) for _ in range(G)]
+    B = np.stack([b for b, _ in Bs])
+    sB = np.stack([s for _, s in Bs])
+    dt = torch.bfloat16 if out else torch.float32
+    C = torch.full((R, N), 7.0, dtype=dt, device="cuda")
+    mxq.grouped_scaled_gemm(dev_u8(A), fa, dev_u8(sA), ma, dev_u8(B), fb, dev_u8(sB), mb,
+                            torch.from_numpy(off).cuda(), G, R, N, K, C, out=mxq.OUT_BF16 if out else mxq.OUT_F32)
+    Ch = host(C)
+    for gi in range(G):
+        r0, r1 = int(off[gi]), int(off[gi + 1])
+        if r1 == r0:
+            continue
+        Cg = run(np.ascontiguousarray(A[r0:r1]), fa, np.ascontiguousarray(sA[r0:r1]), ma, B[gi], fb, sB[gi], mb,
+                 r1 - r0, N, K, out=mxq.OUT_BF16 if out else 0)
+        view = np.uint16 if out else np.uint32
+        assert np.array_equal(Ch[r0:r1].view(view), Cg.view(view)), f"group {gi}: grouped != dense"
+    if out == 0:
+        m, n = sample_entries(g, R, N, 2500, tile=320)
+        c, cabs = O.grouped_gemm_entries(A, fa, sA, ma, B, fb, sB, mb, off, N, K, m, n)
+        hb = None
+        if not (fa == 2 and fb == 2):
+            hb = np.empty(len(m))
+            for gi in range(G):
+                r0, r1 = int(off[gi]), int(off[gi + 1])
+                sel = (m >= r0) & (m < r1)
+                if sel.any():
+                    hb[sel] = mfma_bound(A[r0:r1], fa, sA[r0:r1], ma, B[gi], fb, sB[gi], mb, K, m[sel] - r0, n[sel])
+        r = check_gemm(Ch[m, n].astype(np.float64), c, cabs, f"grouped 320x192 f{fa}{fb} m{ma}{mb}", hw_bound=hb)
+        log(f"grouped 320x192 f{fa}{fb} m{ma}{mb}: ratio {r:.3f}")
