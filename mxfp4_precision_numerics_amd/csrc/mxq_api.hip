@@ -184,7 +184,7 @@ int mxq_grouped_scaled_gemm(const uint8_t* A, int fa, const void* sA, int ma, co
     if (st != MXQ_OK) return st;
     if (!group_off) return MXQ_ERR_NULL;
     if (!aligned4(group_off)) return MXQ_ERR_ALIGN;
-    if (((total_rows + 127) / 128 + G) * ((N + 127) / 128) > MAX_GRID_X) return MXQ_ERR_SHAPE;
+    if (((total_rows + 127) / 128 + G + 7) * ((N + 127) / 128) > MAX_GRID_X) return MXQ_ERR_SHAPE;
     if (!below_4gib(total_rows, K, fa, ma) || !below_4gib(N, K, fb, mb)) return MXQ_ERR_SHAPE;
     mxq::GemmArgs a{};
     a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C;
