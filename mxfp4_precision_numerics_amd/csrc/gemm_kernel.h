@@ -84,8 +84,7 @@ struct Tile {
 // another, and read the group's rows of A from that XCD's L2 (the launch
 // rounds the m-tiles up to a multiple of 8).  That cut the C4 up-projection's
 // fetch from 1.82 to 1.23 GB (time within 1%); for the 256-row tiles of the
-// fused and down-projection calls it was 5-11% slower, so they keep the plain
-// order.
+// fused call it was 11% slower, so they keep the plain order.
 template <int BM, int BN>
 __device__ __forceinline__ bool tile_of_block(const GemmArgs& g, Tile& t) {
     const int64_t ntn = (g.N + BN - 1) / BN;
@@ -168,14 +167,22 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // The resource, destination and uniform offset are block-uniform; they are
 // passed through readfirstlane so that they sit in scalar registers even
 // where the compiler cannot prove uniformity (free where it can).
+// STREAM marks the load non-temporal (nt): for bytes that no other tile
+// reads, so that they do not push reused operand lines out of the L2.
 __device__ __forceinline__ v4u uni(const v4u& r) {
     return v4u{(unsigned)__builtin_amdgcn_readfirstlane(r[0]), (unsigned)__builtin_amdgcn_readfirstlane(r[1]),
                (unsigned)__builtin_amdgcn_readfirstlane(r[2]), (unsigned)__builtin_amdgcn_readfirstlane(r[3])};
 }
+template <bool STREAM = false>
 __device__ __forceinline__ void dma16(const v4u& rsrc, uint32_t voff, uint32_t soff, uint32_t dst) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-                 ::"v"(voff), "s"(uni(rsrc)), "s"(__builtin_amdgcn_readfirstlane(dst)),
-                   "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen nt lds"
+                     ::"v"(voff), "s"(uni(rsrc)), "s"(__builtin_amdgcn_readfirstlane(dst)),
+                       "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                     ::"v"(voff), "s"(uni(rsrc)), "s"(__builtin_amdgcn_readfirstlane(dst)),
+                       "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
 
 
@@ -200,7 +207,7 @@ __device__ __forceinline__ void dma16(const v4u& rsrc, uint32_t voff, uint32_t s
 // tile holds gate and up rows of the same 128 intermediate columns, the gate
 // rows of each 64 followed by the up rows of the same 64.  Piece i (8 rows)
 // lies in block i / 2 at rows 32 (i % 2) .. of it.
-template <int RB, int ROWS, bool LANE_UNIT = false, bool GU = false>
+template <int RB, int ROWS, bool LANE_UNIT = false, bool GU = false, bool STREAM = false>
 struct TileLoader {
     static constexpr int CH = RB / 16;
     static constexpr int PER_WAVE = ROWS * RB / 1024 / 4;
@@ -227,9 +234,9 @@ struct TileLoader {
     __device__ __forceinline__ void issue(int i, int64_t unit, uint32_t slot, int wave) const {
         const uint32_t u = (uint32_t)(unit * RB), dst = slot + (uint32_t)(wave + 4 * i) * 1024u;
         if constexpr (LANE_UNIT)
-            dma16(rsrc, off0 + piece(i) + u, 0u, dst);
+            dma16<STREAM>(rsrc, off0 + piece(i) + u, 0u, dst);
         else
-            dma16(rsrc, off0 + piece(i), u, dst);
+            dma16<STREAM>(rsrc, off0 + piece(i), u, dst);
     }
 };
 
@@ -401,8 +408,13 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     // ends with the tile's rows (the group's end), B's with the operand
     // FP4 x FP4 units are two K steps: the last one may run past a row's end
     constexpr bool LU = SU > 2;
+    // The 320-row tiles cover a whole group, so no other tile reads their
+    // B panel (the group's weights): it streams past the L2 (measured on
+    // the 32-expert up-projection: 9% faster; where a group's panel is read
+    // by two 256-row tiles, 6% slower)
+    constexpr bool BSTREAM = BM == 320;
     TileLoader<RBA, BM, LU> ldA;
-    TileLoader<RBB, BN, LU, GU> ldB;
+    TileLoader<RBB, BN, LU, GU, BSTREAM> ldB;
     // gate/up tiles: tile n0 (a multiple of 256) covers intermediate columns
     // n0 / 2 .. + 127, gate rows from n0 / 2, up rows inter further
     const int64_t b_row0 = GU ? t.n0 / 2 : t.n0;
@@ -413,7 +425,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     lsA.init(g.ma, g.sA, g.K, t.m_end, t.m0, wave, lane);
     lsB.init(g.mb, t.sB, g.K, g.N, b_row0, wave, lane, g.inter);
     constexpr int TLA = TileLoader<RBA, BM, LU>::PER_WAVE;
-    constexpr int TL = TLA + TileLoader<RBB, BN, LU, GU>::PER_WAVE;  // tile copies per unit
+    constexpr int TL = TLA + TileLoader<RBB, BN, LU, GU, BSTREAM>::PER_WAVE;  // tile copies per unit
     constexpr int NSC = ScaleLoader<BM>::NPW + ScaleLoader<BN, GU>::NPW;  // scale copies per group
 
     // Scale operand of a fragment row, from the staged dword: the byte for K
@@ -877,14 +889,15 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     // grouped: 256-row tiles once the groups average 192 rows (fewer passes over
     // each expert's weights), else 128-row tiles
     if (a.group_off != nullptr && rows < 192) return launch_tile<FA, FB, 128, 256, PRECISE>(a, st);
-    // Groups of 225-320 rows (an expert's share of a routed batch) and a deep
-    // K: one 320-row tile covers a whole group, where 256-row tiles leave a
-    // second, nearly empty tile per group that streams the group's weight
-    // panel again (320 x 192 keeps the accumulators of 256 x 256 and the same
-    // ring slot).  Measured on 32 groups of 234-280 rows: 6% faster at
-    // K = 7168, 2% slower at K = 2048, where the panels are short.
+    // Groups of 225-320 rows (an expert's share of a routed batch): one
+    // 320-row tile covers a whole group, where 256-row tiles leave a second,
+    // nearly empty tile per group that streams the group's weight panel
+    // again (320 x 192 keeps the accumulators of 256 x 256 and the same ring
+    // slot), and the panel streams past the L2.  Measured on 32 groups of
+    // 234-280 rows: 9% faster at K = 7168 and 5% at K = 2048 than 256-row
+    // tiles (2% slower at K = 2048 before the weights streamed).
     if constexpr (!PRECISE && (FA == E2M1) == (FB == E2M1)) {
-        if (a.group_off != nullptr && rows > 224 && rows <= 320 && a.K >= 4096)
+        if (a.group_off != nullptr && rows > 224 && rows <= 320 && a.K >= 2048)
             return launch_tile<FA, FB, 320, 192, false>(a, st);
     }
     if (a.group_off == nullptr) {

@@ -172,15 +172,16 @@ def test_grouped_gemm_mxfp4_k7168(sizes):
     log(f"grouped MXFP4 K=7168 sizes {sizes}: ratio {r:.3f}")
 
 
-@pytest.mark.parametrize("fa,fb,ma,mb,out", [(0, 0, 1, 1, 0), (1, 0, 2, 1, 0), (0, 1, 1, 2, 1), (2, 2, 1, 1, 0)])
-def test_grouped_gemm_320x192_tiles(fa, fb, ma, mb, out):
+@pytest.mark.parametrize("fa,fb,ma,mb,out,K", [(0, 0, 1, 1, 0, 4224), (1, 0, 2, 1, 0, 4224), (0, 1, 1, 2, 1, 4224),
+                                                (2, 2, 1, 1, 0, 4224), (0, 0, 1, 1, 1, 2176), (2, 2, 2, 1, 0, 2304)])
+def test_grouped_gemm_320x192_tiles(fa, fb, ma, mb, out, K):
     """Groups of 300, 0, 250, 331, 229 and 280 rows (average 232: 320 x 192
     tiles; the 331-row group takes a 320-row and an 11-row tile), N = 504 (the
     last n-tile holds 120 columns), K = 4224 (33 K steps through a two-slot
-    ring; the tile serves K >= 4096), fp32 or bf16 output."""
+    ring), 2176 or 2304 (the tile serves K >= 2048), fp32 or bf16 output."""
     sizes = [300, 0, 250, 331, 229, 280]
-    g = np.random.Generator(np.random.PCG64([2300, fa, fb, ma, mb, out]))
-    G, N, K = len(sizes), 504, 4224
+    g = np.random.Generator(np.random.PCG64([2300, fa, fb, ma, mb, out, K]))
+    G, N = len(sizes), 504
     off = np.zeros(G + 1, np.int64)
     off[1:] = np.cumsum(sizes)
     R = int(off[-1])
