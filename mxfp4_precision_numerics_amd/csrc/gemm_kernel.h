@@ -139,7 +139,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 // A block-uniform 64-bit value moved to scalar registers.
 __device__ __forceinline__ int64_t uni64(int64_t v) {
@@ -202,19 +201,24 @@ __device__ __forceinline__ void dma16(const v4u& rsrc, uint32_t voff, uint32_t s
 // when K % 256 == 128) must be range-checked on the last row, so there the
 // unit's offset is added to the per-lane offset.
 //
-// GU (gate/up tiles of the expert MLP, 256 rows of 128 bytes): tile rows
-// [64b, 64b + 64) come from operand rows row0 + 64 (b / 2) + .. of the gate
-// half for even b and of the up half (gu bytes further) for odd b, so that a
-// tile holds gate and up rows of the same 128 intermediate columns, the gate
-// rows of each 64 followed by the up rows of the same 64.  Piece i (8 rows)
-// lies in block i / 2 at rows 32 (i % 2) .. of it.
-template <int RB, int ROWS, bool LANE_UNIT = false, bool GU = false, bool STREAM = false>
+// Gate/up tiles of the expert MLP (GU != 0; 128-byte rows), from operand
+// rows row0 + .. of the gate half and of the up half (gu bytes further):
+//  GU = 1, 256 rows: tile rows [64b, 64b + 64) come from gate rows
+//    row0 + 64 (b / 2) + .. for even b and from the up rows of the same 64
+//    intermediate columns for odd b (128 columns per tile, each wave column
+//    holds gate and up of its own 64).  Piece i (8 rows) lies in block i / 2
+//    at rows 32 (i % 2) .. of it.
+//  GU = 2, 192 rows: tile rows [0, 96) are gate rows row0 .. row0 + 95,
+//    rows [96, 192) the up rows of the same 96 intermediate columns.
+//    Pieces 0-2 of a wave are gate rows, 3-5 the up rows 96 further on.
+template <int RB, int ROWS, bool LANE_UNIT = false, int GU = 0, bool STREAM = false>
 struct TileLoader {
     static constexpr int CH = RB / 16;
     static constexpr int PER_WAVE = ROWS * RB / 1024 / 4;
     static constexpr int RP = 1024 / RB;  // rows per 1 KiB piece
     static_assert(PER_WAVE >= 1 && ROWS * RB % 4096 == 0, "tile unit must split over 4 waves");
-    static_assert(!GU || (RB == 128 && ROWS == 256), "gate/up tiles are 256 rows of 128 bytes");
+    static_assert(GU == 0 || (GU == 1 && RB == 128 && ROWS == 256) || (GU == 2 && RB == 128 && ROWS == 192),
+                  "gate/up tiles are 256 or 192 rows of 128 bytes");
     v4u rsrc;
     uint32_t off0, step, gu;  // lane offset of piece 0; bytes between pieces; gate -> up
     __device__ __forceinline__ void init(const uint8_t* base, int64_t bytes, int64_t ld, int64_t row0, int wave,
@@ -227,8 +231,10 @@ struct TileLoader {
         gu = (uint32_t)(gu_rows * ld);
     }
     __device__ __forceinline__ uint32_t piece(int i) const {
-        if constexpr (GU)
+        if constexpr (GU == 1)
             return (uint32_t)(2 * (i / 4) + (i % 2)) * step + (uint32_t)((i / 2) & 1) * gu;
+        else if constexpr (GU == 2)
+            return (uint32_t)(i % 3) * step + (uint32_t)(i / 3) * gu;
         else
             return (uint32_t)i * step;
     }
@@ -253,16 +259,17 @@ struct TileLoader {
 // drops any dword that is not wholly inside the range, so a BLK128 array
 // whose size is not a multiple of 4 gets a range rounded up to the end of its
 // last aligned dword: the last row's bytes arrive, the (unused) padding bytes
-// share that dword's page.  GU: the tile rows of TileLoader's gate/up mode
-// (wave w copies block w).
+// share that dword's page.  GU: the tile rows of TileLoader's gate/up modes
+// (GU = 1: wave w copies block w; GU = 2: tile row r is a gate row below 96,
+// else an up row).
 constexpr int SG = 4;
-template <int ROWS, bool GU = false>
+template <int ROWS, int GU = 0>
 struct ScaleLoader {
     static constexpr int NCH = (ROWS + 63) / 64;     // chunks of 64 rows
     static constexpr int NPW = (NCH + 3) / 4;        // copies per wave
     static constexpr int SROWS = NCH * 64;           // rows of staging room
     static_assert(ROWS % 32 == 0 && NCH >= 2, "scale rows");
-    static_assert(!GU || ROWS == 256, "gate/up tiles are 256 rows");
+    static_assert(GU == 0 || (GU == 1 && ROWS == 256) || (GU == 2 && ROWS == 192), "gate/up tiles are 256 or 192 rows");
     v4u rsrc;
     uint32_t off[NPW], kmul, mask;
     int dst[NPW];  // byte offsets of this wave's chunks within the operand's part of the slot
@@ -277,8 +284,10 @@ struct ScaleLoader {
             const int ch = (wave + 4 * c) < NCH ? wave + 4 * c : wave % NCH;
             const int r = ch * 64;
             dst[c] = r * 16;
-            const int64_t grow = GU ? row0 + 64 * (wave / 2) + (wave % 2) * gu_rows : row0 + r;
-            off[c] = (uint32_t)((grow + lane) * pitch);
+            int64_t grow = row0 + r + lane;
+            if constexpr (GU == 1) grow = row0 + 64 * (wave / 2) + (wave % 2) * gu_rows + lane;
+            if constexpr (GU == 2) grow = r + lane < 96 ? row0 + r + lane : row0 + gu_rows + r + lane - 96;
+            off[c] = (uint32_t)(grow * pitch);
         }
     }
     __device__ __forceinline__ void issue(int64_t grp, uint32_t slot) const {
@@ -338,17 +347,22 @@ constexpr int copies_after(int J, int NSL, int SU, int TL, int JS, int NSC) {
 // products in fp32.  Slower than the block-scaled FP8 MFMA, whose products
 // are truncated to 13 fractional bits inside each run of 8 K positions.
 //
-// HF >= 0 (the expert MLP's up-projection; grouped, FP8 operands, BN = 256):
-// B tiles hold gate and up rows of 128 intermediate columns (TileLoader's GU
-// mode), so each wave's accumulators hold gate in fragments 0, 1 and up of
-// the same columns in 2, 3 (same lanes, same registers).  The epilogue forms
-// h = silu(gate) * up in binary32 and writes h MX block-32 quantized to
-// format HF (q_out, s_out) instead of C.
+// HF >= 0 (the expert MLP's up-projection; grouped, FP8 operands): B tiles
+// hold gate and up rows of the same intermediate columns (TileLoader's
+// gate/up modes).  The epilogue forms h = silu(gate) * up in binary32 and
+// writes h MX block-32 quantized to format HF (q_out, s_out) instead of C.
+//  * BN = 256 (GU = 1): 128 intermediate columns per tile; each wave's
+//    accumulators hold gate in fragments 0, 1 and up of the same columns in
+//    2, 3 (same lanes, same registers).
+//  * BN = 192 with BM = 320 (GU = 2): 96 intermediate columns per tile; the
+//    waves of column 0 hold gate, those of column 1 the up values of the
+//    same columns, and the epilogue pairs them through LDS.
 template <int FA, int FB, int BM, int BN, bool PRECISE = false, int HF = -1>
 __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     static_assert(!PRECISE || (FA != E2M1 && FB != E2M1), "precise mode takes FP8 operands");
-    constexpr bool GU = HF >= 0;
-    static_assert(!GU || (BN == 256 && FA != E2M1 && FB != E2M1 && !PRECISE), "gate/up epilogue configuration");
+    constexpr int GU = HF < 0 ? 0 : (BN == 256 ? 1 : 2);
+    static_assert(GU == 0 || ((BN == 256 || (BM == 320 && BN == 192)) && FA != E2M1 && FB != E2M1 && !PRECISE),
+                  "gate/up epilogue configuration");
     constexpr int SM = BM / 2, SN = BN / 2;                // a wave's sub-tile (2 x 2 waves)
     using IA = OpInfo<FA>;
     using IB = OpInfo<FB>;
@@ -416,8 +430,8 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     constexpr bool BSTREAM = BM == 320;
     TileLoader<RBA, BM, LU> ldA;
     TileLoader<RBB, BN, LU, GU, BSTREAM> ldB;
-    // gate/up tiles: tile n0 (a multiple of 256) covers intermediate columns
-    // n0 / 2 .. + 127, gate rows from n0 / 2, up rows inter further
+    // gate/up tiles: tile n0 (a multiple of BN) covers intermediate columns
+    // n0 / 2 .. + BN / 2 - 1, gate rows from n0 / 2, up rows inter further
     const int64_t b_row0 = GU ? t.n0 / 2 : t.n0;
     ldA.init(g.A, t.m_end * lda, lda, t.m0, wave, lane);
     ldB.init(t.B, g.N * ldb, ldb, b_row0, wave, lane, g.inter);
@@ -779,7 +793,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
                     if (rr < mlim && (!IDLE || lane < RPI * CPR)) {
                         T* dst = cw + (int64_t)rr * g.ldc + cc;
                         if (cc + PER <= nlim) {
-                            __builtin_nontemporal_store(__builtin_bit_cast(v4u, d), reinterpret_cast<v4u*>(dst));
+                            st_nt16(dst, d);
                         } else {
                             const T* e = reinterpret_cast<const T*>(&d);
 #pragma unroll
@@ -791,7 +805,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
                 __syncthreads();
             }
     };
-    if constexpr (GU) {
+    if constexpr (GU == 1) {
         // Expert MLP epilogue.  The wave's 64 intermediate columns: fragment
         // jj < 2 of a row band holds gate columns 32 jj + l % 32, jj + 2 the
         // up values of the same columns.  Per 32-row band: h in binary32 is
@@ -833,8 +847,64 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
                 const int rr = 32 * i + br;
                 if (rr < mlim) {
                     const int64_t row = row_base + rr;
-                    __builtin_nontemporal_store(v2u{lo, hi}, reinterpret_cast<v2u*>(g.q_out + row * g.inter + hcol + 8 * ch));
+                    st_nt8(g.q_out + row * g.inter + hcol + 8 * ch, make_uint2(lo, hi));
                     if ((lane & 3) == 0) g.s_out[row * spr + (hcol + 8 * ch) / 32] = sb;
+                }
+            }
+            __syncthreads();
+        }
+    } else if constexpr (GU == 2) {
+        // Expert MLP epilogue of the 320 x 192 tile.  Waves of column 0 hold
+        // gate, those of column 1 the up values of the same 96 intermediate
+        // columns (fragment jj: columns 32 jj + l % 32).  Per 32-row band
+        // (fragment row i of both wave rows) every wave stages its values in
+        // LDS (binary32 rows of 104 floats: the two half-waves' rows, 4
+        // apart, fall on disjoint banks); then each of the 256 lanes takes 8
+        // consecutive columns of one row, three times over the band's 64
+        // rows x 12 column chunks, so that a quad of lanes holds one MX block
+        // of 32, and forms h = silu(gate) * up and its codes (the same
+        // arithmetic as the standalone activation kernel on binary32 input).
+        static_assert(FM == 5 && FN == 3, "320 x 192 gate/up tile");
+        constexpr int HP = 104;  // floats per staged row
+        static_assert(4 * 32 * HP * 4 <= SLOT, "epilogue band");
+        float* band = reinterpret_cast<float*>(s0);  // [wave row][wave column][32][HP]
+        float* mineb = band + (wm * 2 + wn) * 32 * HP;
+        const int64_t hcol0 = t.n0 / 2;  // first intermediate column of the tile
+        const int64_t spr = g.inter / 32;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mineb[(8 * (r / 4) + 4 * gq + (r % 4)) * HP + 32 * jj + (lane & 31)] = acc[i][jj][r] * alpha;
+            __syncthreads();
+#pragma unroll
+            for (int pass = 0; pass < 3; ++pass) {
+                const int task = pass * NT + tid;  // 64 rows x 12 chunks of 8 columns
+                const int row = task / 12, ch = task % 12;
+                const int wr = row >> 5, br = row & 31;
+                const float* gp = band + ((wr * 2) * 32 + br) * HP + 8 * ch;
+                const float* up = gp + 32 * HP;
+                const uint4 g0 = *reinterpret_cast<const uint4*>(gp), g1 = *reinterpret_cast<const uint4*>(gp + 4);
+                const uint4 u0 = *reinterpret_cast<const uint4*>(up), u1 = *reinterpret_cast<const uint4*>(up + 4);
+                const uint32_t gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                const uint32_t uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                uint32_t h[8], m = 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    h[k] = as_uint(swiglu_f32(as_float(gv[k]), as_float(uv[k])));
+                    const uint32_t v = h[k] & 0x7FFFFFFFu;
+                    m = m > v ? m : v;
+                }
+                m = quad_max_u32(m);  // lanes 4q .. 4q+3: one row's 32-column block
+                uint32_t lo, hi;
+                uint8_t sb;
+                mx_codes_row8<HF>(h, m, lo, hi, sb);
+                const int64_t row_g = t.m0 + wr * SM + 32 * i + br, col = hcol0 + 8 * ch;
+                if (row_g < t.m_end && col < g.inter) {
+                    st_nt8(g.q_out + row_g * g.inter + col, make_uint2(lo, hi));
+                    if ((lane & 3) == 0) g.s_out[row_g * spr + col / 32] = sb;
                 }
             }
             __syncthreads();
@@ -870,15 +940,18 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
 }
 
 // The expert MLP's up-projection with the SwiGLU + MX epilogue (grouped, FP8
-// operands, native mode): 256-row tiles once the groups average 192 rows.
+// operands, native mode): 256-row tiles once the groups average 192 rows,
+// and for groups of 225-320 rows at K >= 2048 the 320 x 192 tile of the
+// plain grouped GEMM (one tile per group and 96 intermediate columns).
+template <int FA, int FB, int HF>
+hipError_t launch_swiglu_h(const GemmArgs& a, hipStream_t st) {
+    const int64_t rows = a.M / (a.G > 0 ? a.G : 1);
+    if (rows > 224 && rows <= 320 && a.K >= 2048) return launch_tile<FA, FB, 320, 192, false, HF>(a, st);
+    return rows < 192 ? launch_tile<FA, FB, 128, 256, false, HF>(a, st) : launch_tile<FA, FB, 256, 256, false, HF>(a, st);
+}
 template <int FA, int FB>
 hipError_t launch_swiglu_t(const GemmArgs& a, hipStream_t st) {
-    const int64_t rows = a.M / (a.G > 0 ? a.G : 1);
-    if (a.hfmt == E5M2)
-        return rows < 192 ? launch_tile<FA, FB, 128, 256, false, E5M2>(a, st)
-                          : launch_tile<FA, FB, 256, 256, false, E5M2>(a, st);
-    return rows < 192 ? launch_tile<FA, FB, 128, 256, false, E4M3>(a, st)
-                      : launch_tile<FA, FB, 256, 256, false, E4M3>(a, st);
+    return a.hfmt == E5M2 ? launch_swiglu_h<FA, FB, E5M2>(a, st) : launch_swiglu_h<FA, FB, E4M3>(a, st);
 }
 
 // Tile choice: the largest tiles (most operand reuse per LDS byte) unless

@@ -214,7 +214,7 @@ int mxq_grouped_gemm_swiglu_quantize_mx(const uint8_t* A, int fa, const void* sA
     if (!group_off || !s_out) return MXQ_ERR_NULL;
     if (!aligned4(group_off)) return MXQ_ERR_ALIGN;
     const int64_t N = 2 * inter;
-    if (((total_rows + 127) / 128 + G) * ((N + 255) / 256) > MAX_GRID_X) return MXQ_ERR_SHAPE;
+    if (((total_rows + 127) / 128 + G + 7) * ((N + 127) / 128) > MAX_GRID_X) return MXQ_ERR_SHAPE;
     if (!below_4gib(total_rows, K, fa, ma) || !below_4gib(N, K, fb, mb)) return MXQ_ERR_SHAPE;
     mxq::GemmArgs a{};
     a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = nullptr;

@@ -89,18 +89,24 @@ def run_fused_and_chain(A, fa, sA, ma, B, fb, sB, mb, off, R, inter, K, hfmt):
 
 
 CASES = [
-    # (sizes, fa, ma, fb, mb, hfmt): 128-row tiles (groups average < 192 rows) and 256-row tiles
-    ([260, 0, 130, 77, 33], 0, 1, 0, 1, 0),
-    ([300, 250, 0, 280, 190], 0, 1, 0, 1, 0),
-    ([300, 250, 0, 280, 190], 0, 2, 0, 1, 1),
-    ([201, 0, 317, 260], 1, 0, 0, 0, 0),
+    # (sizes, fa, ma, fb, mb, hfmt, inter, K): 128-row tiles (groups average
+    # < 192 rows) and 256-row tiles at K = 512; 320 x 192 tiles (groups
+    # averaging 225-320 rows, K >= 2048: 96 intermediate columns per tile, so
+    # inter = 256 and 128 end in a partial tile, 384 does not)
+    ([260, 0, 130, 77, 33], 0, 1, 0, 1, 0, 256, 512),
+    ([300, 250, 0, 280, 190], 0, 1, 0, 1, 0, 256, 512),
+    ([300, 250, 0, 280, 190], 0, 2, 0, 1, 1, 256, 512),
+    ([201, 0, 317, 260], 1, 0, 0, 0, 0, 256, 512),
+    ([300, 250, 0, 280, 331, 240], 0, 1, 0, 1, 0, 256, 2048),
+    ([300, 250, 0, 280, 331, 240], 0, 2, 1, 1, 1, 384, 2176),
+    ([260, 0, 317, 229], 1, 0, 0, 0, 0, 128, 2048),
 ]
 
 
-@pytest.mark.parametrize("sizes,fa,ma,fb,mb,hfmt", CASES)
-def test_fused_up_projection_swiglu(sizes, fa, ma, fb, mb, hfmt):
-    g = np.random.Generator(np.random.PCG64([3000, len(sizes), fa, ma, fb, mb, hfmt]))
-    G, inter, K = len(sizes), 256, 512
+@pytest.mark.parametrize("sizes,fa,ma,fb,mb,hfmt,inter,K", CASES)
+def test_fused_up_projection_swiglu(sizes, fa, ma, fb, mb, hfmt, inter, K):
+    g = np.random.Generator(np.random.PCG64([3000, len(sizes), fa, ma, fb, mb, hfmt, inter, K]))
+    G = len(sizes)
     off = np.zeros(G + 1, np.int64)
     off[1:] = np.cumsum(sizes)
     R = int(off[-1]) + 9  # trailing rows outside every group stay untouched

@@ -13,7 +13,7 @@ a tile, rows outside every group), widths and depths.
 import numpy as np
 import pytest
 import torch
-from hypothesis import HealthCheck, given, settings
+from hypothesis import HealthCheck, example, given, settings
 from hypothesis import strategies as st
 
 import oracle as O
@@ -89,9 +89,12 @@ def test_grouped_gemm_generated(sizes, n, k, fmts, tail, seed):
 
 
 @SET
-@given(sizes=sizes_st, inter=st.sampled_from([128, 256]), k=st.sampled_from([128, 256, 512]),
+@given(sizes=sizes_st, inter=st.sampled_from([128, 256]), k=st.sampled_from([128, 256, 512, 2048]),
        ma=st.sampled_from([1, 2]), hfmt=st.sampled_from([0, 1]), tail=st.integers(0, 40),
        seed=st.integers(0, 2 ** 31))
+# groups averaging 225-320 rows at K >= 2048: the 320 x 192 tiles
+@example(sizes=[300, 251, 0, 290, 290], inter=256, k=2048, ma=1, hfmt=0, tail=7, seed=5)
+@example(sizes=[233, 299], inter=128, k=2048, ma=2, hfmt=1, tail=0, seed=6)
 def test_fused_up_projection_generated(sizes, inter, k, ma, hfmt, tail, seed):
     g = np.random.Generator(np.random.PCG64(seed))
     G = len(sizes)
