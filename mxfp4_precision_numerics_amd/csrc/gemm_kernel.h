@@ -357,7 +357,7 @@ constexpr int copies_after(int J, int NSL, int SU, int TL, int JS, int NSC) {
 //  * BN = 192 with BM = 320 (GU = 2): 96 intermediate columns per tile; the
 //    waves of column 0 hold gate, those of column 1 the up values of the
 //    same columns, and the epilogue pairs them through LDS.
-template <int FA, int FB, int BM, int BN, bool PRECISE = false, int HF = -1>
+template <int FA, int FB, int BM, int BN, bool PRECISE = false, int HF = -1, bool SKIP = false>
 __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     static_assert(!PRECISE || (FA != E2M1 && FB != E2M1), "precise mode takes FP8 operands");
     constexpr int GU = HF < 0 ? 0 : (BN == 256 ? 1 : 2);
@@ -414,10 +414,15 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     const int64_t pA = g.ma == 1 ? g.K / 32 : g.K / 128;  // scale pitch of the operand rows
     const int64_t pB = g.mb == 1 ? g.K / 32 : g.K / 128;
     const int rA = wm * SM + (lane & 31), rB = wn * SN + (lane & 31);
-    // FP8 / FP4 MFMA: fragments of rows that all lie past the tile's last row
-    // (a group's partial tile, the last m-tile) are neither read nor multiplied
-    const int fact = __builtin_amdgcn_readfirstlane(
-        (int)max(min((t.m_end - (t.m0 + wm * SM) + 31) / 32, (int64_t)FM), (int64_t)0));
+    // SKIP (grouped calls on tiles of up to 256 rows, where a group's last
+    // tile may hold a few rows): fragments of rows that all lie past the
+    // tile's last row are neither read nor multiplied by the FP8 / FP4 MFMA.
+    // Elsewhere every fragment is multiplied (rows past the end read zero and
+    // their outputs are not stored): the per-fragment branches cost the FP4
+    // loops 5-8% and gain nothing where the tile's other wave row is full.
+    const int fact = SKIP ? __builtin_amdgcn_readfirstlane(
+                                (int)max(min((t.m_end - (t.m0 + wm * SM) + 31) / 32, (int64_t)FM), (int64_t)0))
+                          : FM;
 
     // operand extents for the buffer resources (validated below 4 GiB): A's
     // ends with the tile's rows (the group's end), B's with the operand
@@ -930,12 +935,12 @@ inline int64_t cu_count() {
     return n;
 }
 
-template <int FA, int FB, int BM, int BN, bool PRECISE, int HF = -1>
+template <int FA, int FB, int BM, int BN, bool PRECISE, int HF = -1, bool SKIP = false>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
     const int64_t ntn = (a.N + BN - 1) / BN;
     int64_t ntm = (a.group_off == nullptr) ? (a.M + BM - 1) / BM : (a.M + BM - 1) / BM + a.G;
     if (BM == 320 && a.group_off != nullptr) ntm = (ntm + 7) / 8 * 8;  // whole XCD rounds (tile_of_block)
-    hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE, HF>), dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE, HF, SKIP>), dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a);
     return hipGetLastError();
 }
 
@@ -947,7 +952,8 @@ template <int FA, int FB, int HF>
 hipError_t launch_swiglu_h(const GemmArgs& a, hipStream_t st) {
     const int64_t rows = a.M / (a.G > 0 ? a.G : 1);
     if (rows > 224 && rows <= 320 && a.K >= 2048) return launch_tile<FA, FB, 320, 192, false, HF>(a, st);
-    return rows < 192 ? launch_tile<FA, FB, 128, 256, false, HF>(a, st) : launch_tile<FA, FB, 256, 256, false, HF>(a, st);
+    return rows < 192 ? launch_tile<FA, FB, 128, 256, false, HF, true>(a, st)
+                      : launch_tile<FA, FB, 256, 256, false, HF, true>(a, st);
 }
 template <int FA, int FB>
 hipError_t launch_swiglu_t(const GemmArgs& a, hipStream_t st) {
@@ -960,12 +966,14 @@ template <int FA, int FB, bool PRECISE>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     static_assert(!PRECISE || (FA != E2M1 && FB != E2M1), "precise mode takes FP8 operands");
     const int64_t rows = a.group_off ? (a.M / (a.G > 0 ? a.G : 1)) : a.M;
-    if (rows <= 160 || a.N < 256) return launch_tile<FA, FB, 128, 128, PRECISE>(a, st);
+    constexpr bool SK = !PRECISE;  // grouped tiles of up to 256 rows skip fragments past a group's end
+    if (rows <= 160 || a.N < 256)
+        return a.group_off ? launch_tile<FA, FB, 128, 128, PRECISE, -1, SK>(a, st) : launch_tile<FA, FB, 128, 128, PRECISE>(a, st);
     const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
     if (a.group_off == nullptr && t256 < 192) return launch_tile<FA, FB, 128, 128, PRECISE>(a, st);
     // grouped: 256-row tiles once the groups average 192 rows (fewer passes over
     // each expert's weights), else 128-row tiles
-    if (a.group_off != nullptr && rows < 192) return launch_tile<FA, FB, 128, 256, PRECISE>(a, st);
+    if (a.group_off != nullptr && rows < 192) return launch_tile<FA, FB, 128, 256, PRECISE, -1, SK>(a, st);
     // Groups of 225-320 rows (an expert's share of a routed batch): one
     // 320-row tile covers a whole group, where 256-row tiles leave a second,
     // nearly empty tile per group that streams the group's weight panel
@@ -997,7 +1005,7 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
             return launch_tile<FA, FB, 128, 256, PRECISE>(a2, st);
         }
     }
-    return launch_tile<FA, FB, 256, 256, PRECISE>(a, st);
+    return a.group_off ? launch_tile<FA, FB, 256, 256, PRECISE, -1, SK>(a, st) : launch_tile<FA, FB, 256, 256, PRECISE>(a, st);
 }
 
 }  // namespace mxq
