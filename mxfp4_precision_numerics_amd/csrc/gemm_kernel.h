@@ -358,7 +358,7 @@ constexpr int copies_after(int J, int NSL, int SU, int TL, int JS, int NSC) {
 //  * BN = 192 with BM = 320 (GU = 2): 96 intermediate columns per tile; the
 //    waves of column 0 hold gate, those of column 1 the up values of the
 //    same columns, and the epilogue pairs them through LDS.
-template <int FA, int FB, int BM, int BN, bool PRECISE = false, int HF = -1, bool SKIP = false, bool B32 = false>
+template <int FA, int FB, int BM, int BN, bool PRECISE = false, int HF = -1, bool SKIP = false, int SMS = -1>
 __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     static_assert(!PRECISE || (FA != E2M1 && FB != E2M1), "precise mode takes FP8 operands");
     constexpr int GU = HF < 0 ? 0 : (BN == 256 ? 1 : 2);
@@ -412,10 +412,11 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     const int64_t ldb = (FB == E2M1) ? g.K / 2 : g.K;
     const int64_t nks = g.K / 128, H = 2 * nks;         // K steps, K halves
     const int gq = lane >> 5;                            // K block of the instruction this lane feeds
-    // B32: both operands carry BLK32 scales (known at compile time, so the
-    // scale operands are the staged dwords themselves, with no per-step
-    // mode arithmetic)
-    const int gma = B32 ? 1 : g.ma, gmb = B32 ? 1 : g.mb;
+    // SMS >= 0: both operands carry scales of that mode, known at compile
+    // time.  BLK32 (1): the scale operands are the staged dwords themselves,
+    // with no per-step mode arithmetic; per-tensor (0): no scale bytes are
+    // staged or read at all (the operands' factors act in the epilogue).
+    const int gma = SMS >= 0 ? SMS : g.ma, gmb = SMS >= 0 ? SMS : g.mb;
     const int64_t pA = gma == 1 ? g.K / 32 : g.K / 128;  // scale pitch of the operand rows
     const int64_t pB = gmb == 1 ? g.K / 32 : g.K / 128;
     const int rA = wm * SM + (lane & 31), rB = wn * SN + (lane & 31);
@@ -451,7 +452,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     lsB.init(gmb, t.sB, g.K, g.N, b_row0, wave, lane, g.inter);
     constexpr int TLA = TileLoader<RBA, BM, LU>::PER_WAVE;
     constexpr int TL = TLA + TileLoader<RBB, BN, LU, GU, BSTREAM>::PER_WAVE;  // tile copies per unit
-    constexpr int NSC = ScaleLoader<BM>::NPW + ScaleLoader<BN, GU>::NPW;  // scale copies per group
+    constexpr int NSC = SMS == 0 ? 0 : ScaleLoader<BM>::NPW + ScaleLoader<BN, GU>::NPW;  // scale copies per group
 
     // Scale operand of a fragment row, from the staged dword: the byte for K
     // half h ends up at byte 2h (BLK32: blocks 2h + gq; BLK128: the step's
@@ -582,9 +583,11 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
     };
     // Scale group u (K steps 4u .. 4u+3) into scale slot u % 2.
     auto issue_scales = [&](int64_t grp) __attribute__((always_inline)) {
-        const uint32_t cs = LC0 + (uint32_t)(grp & 1) * (LC1 - LC0);  // (a select here defeats SROA)
-        lsA.issue(grp, cs);
-        lsB.issue(grp, cs + 16u * SRA);
+        if constexpr (SMS != 0) {
+            const uint32_t cs = LC0 + (uint32_t)(grp & 1) * (LC1 - LC0);  // (a select here defeats SROA)
+            lsA.issue(grp, cs);
+            lsB.issue(grp, cs + 16u * SRA);
+        }
     };
     // Schedule: unit v (halves SU*v ..) lives in slot v % NSL.  Its copies are
     // issued in the last half of unit v - NSL, right after that half's
@@ -621,8 +624,8 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
             dst = lds_addr(slot(std::integral_constant<int, CUR>{}));
             if constexpr (J == JS) issue_scales((j + 1 + (NSL - 1) * SU) / (2 * SG));
         }
-        uint32_t da[FM], db[FN];
-        if constexpr (RS) {
+        uint32_t da[FM] = {}, db[FN] = {};
+        if constexpr (RS && SMS != 0) {
             const int64_t ks = (j + 1) / 2;
             const uint8_t* cs = ((ks / SG) & 1) ? c1 : c0;
             const uint32_t oa = dwA(ks), ob = dwB(ks);
@@ -719,12 +722,14 @@ __global__ void __launch_bounds__(NT, 1) k_gemm(const GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         fa[0][i] = frag_a(s0, i, 0);
-        sa[0][i] = sreg(smA, *reinterpret_cast<const uint32_t*>(c0 + (rA + 32 * i) * 16 + dwA(0)), sshift(smA, shA, 0));
+        sa[0][i] = sreg(smA, SMS == 0 ? 0u : *reinterpret_cast<const uint32_t*>(c0 + (rA + 32 * i) * 16 + dwA(0)),
+                        sshift(smA, shA, 0));
     }
 #pragma unroll
     for (int jj = 0; jj < FN; ++jj) {
         fb[0][jj] = frag_b(s0, jj, 0);
-        sb[0][jj] = sreg(smB, *reinterpret_cast<const uint32_t*>(c0 + 16 * SRA + (rB + 32 * jj) * 16 + dwB(0)), sshift(smB, shB, 0));
+        sb[0][jj] = sreg(smB, SMS == 0 ? 0u : *reinterpret_cast<const uint32_t*>(c0 + 16 * SRA + (rB + 32 * jj) * 16 + dwB(0)),
+                         sshift(smB, shB, 0));
     }
     if constexpr (PRECISE) {
 #pragma unroll
@@ -948,10 +953,16 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
     // both operands BLK32: the precise mode (the mode arithmetic competes
     // with its conversions: 2% faster), FP4 x FP4 (4%) and dense FP8 (1-2%;
     // on the grouped 320-row tiles it measured 1.6% slower)
+    // Both per-tensor (dense FP8 only): no scale staging at all.
     constexpr bool ALL32 = PRECISE || (FA == E2M1 && FB == E2M1);
     constexpr bool CAN32 = ALL32 || (HF < 0 && BM != 320);
+    constexpr bool CAN0 = FA != E2M1 && FB != E2M1 && HF < 0 && BM != 320;
     if (CAN32 && a.ma == 1 && a.mb == 1 && (ALL32 || a.group_off == nullptr))
-        hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE, HF, SKIP, CAN32>), dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE, HF, SKIP, CAN32 ? 1 : -1>), dim3((unsigned)(ntm * ntn)), dim3(NT),
+                           0, st, a);
+    else if (CAN0 && a.ma == 0 && a.mb == 0 && a.group_off == nullptr)
+        hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE, HF, SKIP, CAN0 ? 0 : -1>), dim3((unsigned)(ntm * ntn)), dim3(NT),
+                           0, st, a);
     else
         hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE, HF, SKIP>), dim3((unsigned)(ntm * ntn)), dim3(NT), 0, st, a);
     return hipGetLastError();
