@@ -951,13 +951,13 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
     int64_t ntm = (a.group_off == nullptr) ? (a.M + BM - 1) / BM : (a.M + BM - 1) / BM + a.G;
     if (BM == 320 && a.group_off != nullptr) ntm = (ntm + 7) / 8 * 8;  // whole XCD rounds (tile_of_block)
     // both operands BLK32: the precise mode (the mode arithmetic competes
-    // with its conversions: 2% faster), FP4 x FP4 (4%) and dense FP8 (1-2%;
-    // on the grouped 320-row tiles it measured 1.6% slower)
+    // with its conversions: 2% faster), FP4 x FP4 (4%), dense FP8 (1-2%)
+    // and the grouped 320-row tiles (2% on the down-projection).
     // Both per-tensor (dense FP8 only): no scale staging at all.
     constexpr bool ALL32 = PRECISE || (FA == E2M1 && FB == E2M1);
-    constexpr bool CAN32 = ALL32 || (HF < 0 && BM != 320);
+    constexpr bool CAN32 = ALL32 || HF < 0;
     constexpr bool CAN0 = FA != E2M1 && FB != E2M1 && HF < 0 && BM != 320;
-    if (CAN32 && a.ma == 1 && a.mb == 1 && (ALL32 || a.group_off == nullptr))
+    if (CAN32 && a.ma == 1 && a.mb == 1 && (ALL32 || a.group_off == nullptr || BM == 320))
         hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE, HF, SKIP, CAN32 ? 1 : -1>), dim3((unsigned)(ntm * ntn)), dim3(NT),
                            0, st, a);
     else if (CAN0 && a.ma == 0 && a.mb == 0 && a.group_off == nullptr)
