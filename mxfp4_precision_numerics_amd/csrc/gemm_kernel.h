@@ -955,8 +955,8 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
     // and the grouped 320-row tiles (2% on the down-projection).
     // Both per-tensor (dense FP8 only): no scale staging at all.
     constexpr bool ALL32 = PRECISE || (FA == E2M1 && FB == E2M1);
-    constexpr bool CAN32 = ALL32 || HF < 0;
-    constexpr bool CAN0 = FA != E2M1 && FB != E2M1 && HF < 0 && BM != 320;
+    constexpr bool CAN32 = ALL32 || (HF < 0 && !SKIP);
+    constexpr bool CAN0 = FA != E2M1 && FB != E2M1 && HF < 0 && BM != 320 && !SKIP;
     if (CAN32 && a.ma == 1 && a.mb == 1 && (ALL32 || a.group_off == nullptr || BM == 320))
         hipLaunchKernelGGL((k_gemm<FA, FB, BM, BN, PRECISE, HF, SKIP, CAN32 ? 1 : -1>), dim3((unsigned)(ntm * ntn)), dim3(NT),
                            0, st, a);
