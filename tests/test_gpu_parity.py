@@ -797,24 +797,28 @@ def test_gemm_precise_tiny_operands():
     check_gemm(C, Cref, Cabs, "precise tiny")
 
 
-def test_grouped_gemm_precise():
-    g = np.random.Generator(np.random.PCG64(1700))
+@pytest.mark.parametrize("ma,mb", [(2, 1), (1, 1), (0, 0)])
+def test_grouped_gemm_precise(ma, mb):
+    """Grouped precise mode with BLK128 x BLK32 scales (the general kernel),
+    BLK32 on both operands (the kernel specialised for them) and per-tensor
+    factors on both (one factor for every group's B)."""
+    g = np.random.Generator(np.random.PCG64([1700, ma, mb]))
     G, N, K = 5, 192, 384
     sizes = [40, 0, 131, 7, 64]
     off = np.zeros(G + 1, np.int64)
     off[1:] = np.cumsum(sizes)
     R = int(off[-1])
-    A, sA = rand_operand(g, 0, 2, R, K)
-    Bs = [rand_operand(g, 0, 1, N, K) for _ in range(G)]
+    A, sA = rand_operand(g, 0, ma, R, K)
+    Bs = [rand_operand(g, 0, mb, N, K) for _ in range(G)]
     B = np.stack([b for b, _ in Bs])
-    sB = np.stack([s for _, s in Bs])
+    sB = Bs[0][1] if mb == 0 else np.stack([s for _, s in Bs])
     C = torch.empty((R, N), dtype=torch.float32, device="cuda")
-    mxq.grouped_scaled_gemm(dev_u8(A), 0, dev_u8(sA), 2, dev_u8(B), 0, dev_u8(sB), 1,
+    mxq.grouped_scaled_gemm(dev_u8(A), 0, gemm_scale_arg(sA, ma), ma, dev_u8(B), 0, gemm_scale_arg(sB, mb), mb,
                             torch.from_numpy(off).cuda(), G, R, N, K, C, out=mxq.OUT_PRECISE)
     m_idx = np.repeat(np.arange(R), N)
     n_idx = np.tile(np.arange(N), R)
-    c, cabs = O.grouped_gemm_entries(A, 0, sA, 2, B, 0, sB, 1, off, N, K, m_idx, n_idx)
-    check_gemm(host(C), c.reshape(-1, N), cabs.reshape(-1, N), "grouped precise")
+    c, cabs = O.grouped_gemm_entries(A, 0, sA, ma, B, 0, sB, mb, off, N, K, m_idx, n_idx)
+    check_gemm(host(C), c.reshape(-1, N), cabs.reshape(-1, N), f"grouped precise m{ma}{mb}")
 
 
 @pytest.mark.parametrize("out", [0, 16])
